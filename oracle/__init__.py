@@ -1,0 +1,11 @@
+"""Float64 CPU oracle (test infrastructure only; never used by the product path)."""
+from .attention import (  # noqa: F401
+    allowed,
+    backward,
+    bwd_preprocess,
+    forward,
+    mask_matrix,
+    rows_forward,
+    sample_keys,
+    sample_rows,
+)

@@ -1,0 +1,196 @@
+"""Float64 CPU oracle for scaled-dot-product attention and its gradients.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import this module:
+only the tests, the smoke check and the benchmark's CPU-baseline leg use it.
+It shares no code with the HIP library.
+
+What it computes is the plain definition of attention, written out with
+matrix products and no blocking, fusion or online rescaling:
+
+  S   = scale * Q K^T                      per batch b and query head h, with
+                                           K, V taken from kv head g = h // (Hq/Hkv)
+  S_ij = -inf where the mask forbids (i, j)
+  LSE_i = log sum_j exp(S_ij)              natural log
+  P   = exp(S - LSE)                       exactly 0 at masked entries
+  O   = P V
+  dP  = dO V^T,   Delta_i = sum_d dO_id O_id,   dS = P * (dP - Delta)
+  dQ  = scale * dS K,  dK_g = scale * sum_{h in g} dS^T Q,  dV_g = sum_{h in g} P^T dO
+
+Sources (the pages this follows):
+  * mlx-bun flash-attention.ts, `manualSdpa`: materialised GQA attention,
+    q reshaped to [B, Hkv, reps, T, D] so consecutive query heads share one kv
+    head; scores times scale, masked, softmax, times V.
+  * mlx-bun flash-attention.ts, forward shader: the mask rule (causal
+    `kpos > q_row`; window `W != 0 and q_row >= kpos and q_row - kpos >= W`),
+    the scale applied to the dot product before masking, and the natural-log
+    LSE `m + log(l)` handed to the backward.
+  * mlx-bun flash-attention.ts, D pre-pass and dK/dV / dQ shaders: Delta as
+    the row sum of O*dO, p = exp(s - L), ds = p * (dp - Delta), dV += p dO,
+    dK += ds q scale, dQ += ds k scale.
+  * ggmlR R/ag_flash_attn.R, `.ag_flash_mask`: causal means query j attends to
+    keys 1..j (top-left alignment).
+
+Readings where the pages are silent or disagree (each listed in the design notes):
+  * a row whose every key is masked gets O = 0, LSE = -inf and contributes no
+    gradient (the forward shader would divide 0 by 0 there);
+  * masked probabilities are exactly 0 (true -inf, no clamp of the exponent);
+  * the window counts keys including the query itself: allowed keys are
+    (i - W, i]; without causal it trims only the past, as the shader does.
+
+Pins: every function here is checked in tests/test_oracle_pins.py against
+central finite differences, torch's float64 autograd of a materialised
+attention, closed forms, invariants and brute-force loops on tiny inputs.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def allowed(i: int, j: int, causal: bool, window: int) -> bool:
+    """Mask rule for query row i and key j (forward shader of mlx-bun flash-attention.ts)."""
+    if causal and j > i:
+        return False
+    if window != 0 and i >= j and i - j >= window:
+        return False
+    return True
+
+
+def mask_matrix(rows, Lkv: int, causal: bool, window: int, cols=None) -> np.ndarray:
+    """Boolean [len(rows), len(cols)]: True where query row i may attend key j.
+
+    cols defaults to all keys 0..Lkv-1.
+    """
+    i = np.asarray(rows, dtype=np.int64)[:, None]
+    j = (np.arange(Lkv, dtype=np.int64) if cols is None else np.asarray(cols, dtype=np.int64))[None, :]
+    ok = np.ones((i.shape[0], j.shape[1]), dtype=bool)
+    if causal:
+        ok &= j <= i
+    if window != 0:
+        ok &= ~((i >= j) & (i - j >= window))
+    return ok
+
+
+def _kv_head(h: int, Hq: int, Hkv: int) -> int:
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return h // (Hq // Hkv)
+
+
+def rows_forward(q_rows, K, V, rows, scale, causal, window):
+    """Forward for a set of query rows of one (b, h).
+
+    q_rows [R, D], K and V [Lkv, D], rows = the R absolute row indices.
+    Returns S (masked, -inf where forbidden), P, O [R, D], LSE [R].
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    S = scale * (q_rows @ K.T)
+    ok = mask_matrix(rows, K.shape[0], causal, window)
+    S = np.where(ok, S, -np.inf)
+    m = S.max(axis=1)
+    live = np.isfinite(m)
+    m0 = np.where(live, m, 0.0)
+    with np.errstate(under="ignore"):
+        total = np.exp(S - m0[:, None]).sum(axis=1)
+    lse = np.where(live, m0 + np.log(np.where(live, total, 1.0)), -np.inf)
+    lse0 = np.where(live, lse, 0.0)
+    with np.errstate(under="ignore"):
+        P = np.where(ok & live[:, None], np.exp(S - lse0[:, None]), 0.0)
+    O = P @ V
+    return S, P, O, lse
+
+
+def forward(q, k, v, scale, causal=False, window=0):
+    """O [B,Hq,Lq,D] and natural-log LSE [B,Hq,Lq] for float64 inputs."""
+    B, Hq, Lq, D = q.shape
+    Hkv = k.shape[1]
+    O = np.zeros((B, Hq, Lq, v.shape[3]))
+    LSE = np.zeros((B, Hq, Lq))
+    rows = np.arange(Lq)
+    for b in range(B):
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            _, _, O[b, h], LSE[b, h] = rows_forward(q[b, h], k[b, g], v[b, g], rows, scale, causal, window)
+    return O, LSE
+
+
+def bwd_preprocess(o, do):
+    """Delta [.., L] = sum over the last axis of dO * O (mlx-bun flash-attention.ts, D pre-pass)."""
+    return (np.asarray(do, dtype=np.float64) * np.asarray(o, dtype=np.float64)).sum(axis=-1)
+
+
+def backward(q, k, v, do, scale, causal=False, window=0):
+    """Gradients of f = sum(dO * O) with respect to q, k, v.
+
+    Returns dict with O, LSE, Delta, dQ, dK, dV (all float64).
+    """
+    B, Hq, Lq, D = q.shape
+    Hkv, Lkv = k.shape[1], k.shape[2]
+    O = np.zeros((B, Hq, Lq, v.shape[3]))
+    LSE = np.zeros((B, Hq, Lq))
+    Delta = np.zeros((B, Hq, Lq))
+    dQ = np.zeros_like(q, dtype=np.float64)
+    dK = np.zeros((B, Hkv, Lkv, D))
+    dV = np.zeros((B, Hkv, Lkv, v.shape[3]))
+    rows = np.arange(Lq)
+    for b in range(B):
+        for h in range(Hq):  # heads of one group summed in increasing h
+            g = _kv_head(h, Hq, Hkv)
+            Kg, Vg = k[b, g], v[b, g]
+            _, P, Oh, lse = rows_forward(q[b, h], Kg, Vg, rows, scale, causal, window)
+            dOh = do[b, h]
+            dP = dOh @ Vg.T
+            delta = bwd_preprocess(Oh, dOh)
+            dS = P * (dP - delta[:, None])
+            dQ[b, h] = scale * (dS @ Kg)
+            dK[b, g] += scale * (dS.T @ q[b, h])
+            dV[b, g] += P.T @ dOh
+            O[b, h], LSE[b, h], Delta[b, h] = Oh, lse, delta
+    return {"O": O, "LSE": LSE, "Delta": Delta, "dQ": dQ, "dK": dK, "dV": dV}
+
+
+# ---------------------------------------------------------------------------
+# Row / key subsets of the same definition, for shapes too large to
+# materialise whole (e.g. L = 32768): each output element needs only its own
+# row of scores (O, LSE, dQ) or the rows that attend its key (dK, dV).
+# ---------------------------------------------------------------------------
+
+def sample_rows(q, k, v, do, scale, causal, window, b, h, rows):
+    """O, LSE, Delta, dQ for the given query rows of (b, h)."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    g = _kv_head(h, Hq, Hkv)
+    Kg, Vg = k[b, g], v[b, g]
+    rows = np.asarray(rows)
+    _, P, O, lse = rows_forward(q[b, h, rows], Kg, Vg, rows, scale, causal, window)
+    dOr = do[b, h, rows]
+    delta = bwd_preprocess(O, dOr)
+    dS = P * (dOr @ Vg.T - delta[:, None])
+    return {"O": O, "LSE": lse, "Delta": delta, "dQ": scale * (dS @ Kg)}
+
+
+def sample_keys(q, k, v, do, scale, causal, window, b, g, keys):
+    """dK, dV for the given keys of kv head g in batch b.
+
+    Every query row that may attend one of the keys contributes, for every
+    query head of the group; each such row's LSE and Delta come from its own
+    full row of scores.
+    """
+    Hq, Hkv = q.shape[1], k.shape[1]
+    Lq, Lkv = q.shape[2], k.shape[2]
+    reps = Hq // Hkv
+    keys = np.asarray(keys)
+    Kg, Vg = k[b, g], v[b, g]
+    any_ok = mask_matrix(np.arange(Lq), Lkv, causal, window, cols=keys).any(axis=1)
+    rows = np.nonzero(any_ok)[0]
+    dK = np.zeros((len(keys), Kg.shape[1]))
+    dV = np.zeros((len(keys), Vg.shape[1]))
+    if len(rows) == 0:
+        return {"dK": dK, "dV": dV}
+    for r in range(reps):
+        h = g * reps + r
+        _, P, O, lse = rows_forward(q[b, h, rows], Kg, Vg, rows, scale, causal, window)
+        dOr = do[b, h, rows]
+        delta = bwd_preprocess(O, dOr)
+        dS = P * (dOr @ Vg.T - delta[:, None])
+        dK += scale * (dS[:, keys].T @ q[b, h, rows])
+        dV += P[:, keys].T @ dOr
+    return {"dK": dK, "dV": dV}
