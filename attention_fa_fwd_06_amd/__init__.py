@@ -1,0 +1,222 @@
+"""Python binding of libfa.so, the gfx950 FlashAttention-2 training attention.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/fa.h. torch tensors provide the
+device memory and the stream. There is no fallback: if libfa.so is missing
+or fails to load, every call raises.
+
+Low-level calls (same names and argument order as the C ABI; outputs are
+caller-allocated tensors):
+    fa_fwd(q, k, v, o, lse, scale, causal, window)
+    fa_bwd_preprocess(o, do, delta)
+    fa_bwd_dkv(q, k, v, do, lse, delta, dk, dv, scale, causal, window)
+    fa_bwd_dq(q, k, v, do, lse, delta, dq, scale, causal, window)
+Convenience wrappers that allocate their outputs:
+    forward(q, k, v, scale=None, causal=False, window=0) -> (o, lse)
+    backward(q, k, v, o, lse, do, scale=None, causal=False, window=0) -> (dq, dk, dv)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+STATUS = {
+    0: "FA_OK",
+    -1: "FA_ERR_NULL",
+    -2: "FA_ERR_SHAPE",
+    -3: "FA_ERR_HEADDIM",
+    -4: "FA_ERR_DTYPE",
+    -5: "FA_ERR_ALIGN",
+    -6: "FA_ERR_ARG",
+    -7: "FA_ERR_LAUNCH",
+}
+EXPORTS = ("fa_fwd", "fa_bwd_preprocess", "fa_bwd_dkv", "fa_bwd_dq", "fa_status_string")
+
+_lib = None
+
+
+class FaError(ValueError):
+    """A status other than FA_OK returned by libfa.so."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {STATUS.get(status, status)}: {status_string(status)}")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa.so (once) and declare its signatures. Raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m attention_fa_fwd_06_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.fa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, P]
+    lib.fa_bwd_preprocess.argtypes = [P, P, P, I, I, I, I, I, P]
+    lib.fa_bwd_dkv.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, P]
+    lib.fa_bwd_dq.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, P]
+    for fn in ("fa_fwd", "fa_bwd_preprocess", "fa_bwd_dkv", "fa_bwd_dq"):
+        getattr(lib, fn).restype = I
+    lib.fa_status_string.argtypes = [I]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}: use float32, float16 or bfloat16")
+    return codes[t.dtype]
+
+
+def _ptr(t, name, device=None, dtype=None) -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    import torch
+
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise FaError(fn, status)
+
+
+def _shape4(t, name):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-D, got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
+def _attn_shapes(q, k, v):
+    B, Hq, Lq, D = _shape4(q, "q")
+    Bk, Hkv, Lkv, Dk = _shape4(k, "k")
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"v shape {tuple(v.shape)} != k shape {tuple(k.shape)}")
+    if Bk != B or Dk != D:
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree on batch or head dim")
+    return B, Hq, Hkv, Lq, Lkv, D
+
+
+def fa_fwd(q, k, v, o, lse, scale, causal=False, window=0):
+    """O and LSE of softmax attention (see include/fa.h, fa_fwd)."""
+    lib = load_library()
+    B, Hq, Hkv, Lq, Lkv, D = _attn_shapes(q, k, v)
+    import torch
+
+    dev, dt = q.device, q.dtype
+    if tuple(o.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, Lq):
+        raise ValueError("o must match q and lse must be [B, Hq, Lq]")
+    st = lib.fa_fwd(_ptr(q, "q", dev, dt), _ptr(k, "k", dev, dt), _ptr(v, "v", dev, dt), _ptr(o, "o", dev, dt),
+                    _ptr(lse, "lse", dev, torch.float32), B, Hq, Hkv, Lq, Lkv, D, float(scale), int(bool(causal)),
+                    int(window), _dtype_code(q), _stream(dev))
+    _check("fa_fwd", st)
+
+
+def fa_bwd_preprocess(o, do, delta):
+    """delta = rowsum(dO * O) (see include/fa.h, fa_bwd_preprocess)."""
+    lib = load_library()
+    import torch
+
+    B, Hq, Lq, D = _shape4(o, "o")
+    dev, dt = o.device, o.dtype
+    if tuple(do.shape) != tuple(o.shape) or tuple(delta.shape) != (B, Hq, Lq):
+        raise ValueError("dO must match o and delta must be [B, Hq, Lq]")
+    st = lib.fa_bwd_preprocess(_ptr(o, "o", dev, dt), _ptr(do, "dO", dev, dt), _ptr(delta, "delta", dev, torch.float32),
+                               B, Hq, Lq, D, _dtype_code(o), _stream(dev))
+    _check("fa_bwd_preprocess", st)
+
+
+def _bwd_common(q, k, v, do, lse, delta):
+    import torch
+
+    B, Hq, Hkv, Lq, Lkv, D = _attn_shapes(q, k, v)
+    if tuple(do.shape) != tuple(q.shape):
+        raise ValueError("dO must match q")
+    if tuple(lse.shape) != (B, Hq, Lq) or tuple(delta.shape) != (B, Hq, Lq):
+        raise ValueError("lse and delta must be [B, Hq, Lq]")
+    dev, dt = q.device, q.dtype
+    ptrs = [_ptr(q, "q", dev, dt), _ptr(k, "k", dev, dt), _ptr(v, "v", dev, dt), _ptr(do, "dO", dev, dt),
+            _ptr(lse, "lse", dev, torch.float32), _ptr(delta, "delta", dev, torch.float32)]
+    return (B, Hq, Hkv, Lq, Lkv, D), ptrs, dev, dt
+
+
+def fa_bwd_dkv(q, k, v, do, lse, delta, dk, dv, scale, causal=False, window=0):
+    """dK and dV (see include/fa.h, fa_bwd_dkv)."""
+    lib = load_library()
+    dims, ptrs, dev, dt = _bwd_common(q, k, v, do, lse, delta)
+    if tuple(dk.shape) != tuple(k.shape) or tuple(dv.shape) != tuple(k.shape):
+        raise ValueError("dk and dv must match k")
+    st = lib.fa_bwd_dkv(*ptrs, _ptr(dk, "dk", dev, dt), _ptr(dv, "dv", dev, dt), *dims, float(scale),
+                        int(bool(causal)), int(window), _dtype_code(q), _stream(dev))
+    _check("fa_bwd_dkv", st)
+
+
+def fa_bwd_dq(q, k, v, do, lse, delta, dq, scale, causal=False, window=0):
+    """dQ (see include/fa.h, fa_bwd_dq)."""
+    lib = load_library()
+    dims, ptrs, dev, dt = _bwd_common(q, k, v, do, lse, delta)
+    if tuple(dq.shape) != tuple(q.shape):
+        raise ValueError("dq must match q")
+    st = lib.fa_bwd_dq(*ptrs, _ptr(dq, "dq", dev, dt), *dims, float(scale), int(bool(causal)), int(window),
+                       _dtype_code(q), _stream(dev))
+    _check("fa_bwd_dq", st)
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)
+
+
+def forward(q, k, v, scale=None, causal=False, window=0):
+    """Allocate O and LSE and run fa_fwd. Returns (o, lse)."""
+    import torch
+
+    B, Hq, Lq, D = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Lq), device=q.device, dtype=torch.float32)
+    fa_fwd(q, k, v, o, lse, default_scale(D) if scale is None else scale, causal, window)
+    return o, lse
+
+
+def backward(q, k, v, o, lse, do, scale=None, causal=False, window=0, delta=None):
+    """Run the three backward phases. Returns (dq, dk, dv)."""
+    import torch
+
+    B, Hq, Lq, D = q.shape
+    scale = default_scale(D) if scale is None else scale
+    if delta is None:
+        delta = torch.empty((B, Hq, Lq), device=q.device, dtype=torch.float32)
+    fa_bwd_preprocess(o, do, delta)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa_bwd_dkv(q, k, v, do, lse, delta, dk, dv, scale, causal, window)
+    fa_bwd_dq(q, k, v, do, lse, delta, dq, scale, causal, window)
+    return dq, dk, dv

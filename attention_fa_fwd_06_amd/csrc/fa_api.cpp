@@ -1,0 +1,163 @@
+// C-ABI front end: argument checks, head-dim bucket selection, launch.
+//
+// Every check runs before any HIP call, so a bad argument returns a status
+// code without touching the device (ggmlR R/ag_flash_attn.R checks its
+// arguments and raises an error instead of letting the backend abort; the MLX
+// VJP dispatch throws rather than running an unsupported path).
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/fa.h"
+#include "fa_types.hpp"
+
+namespace {
+
+constexpr long long kMaxElems = (1LL << 31) - 1;
+constexpr int kMaxLen = 1 << 24;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+fa_status_t check_dtype(fa_dtype_t dt) {
+    return (dt == FA_F32 || dt == FA_F16 || dt == FA_BF16) ? FA_OK : FA_ERR_DTYPE;
+}
+
+fa_status_t check_headdim(int D, fa_dtype_t dt) {
+    if (D < 32 || D > 512 || D % 8 != 0) return FA_ERR_HEADDIM;
+    if (dt == FA_F32 && D > 256) return FA_ERR_HEADDIM;
+    return FA_OK;
+}
+
+fa_status_t check_attn(int B, int Hq, int Hkv, int Lq, int Lkv, int D, float scale, int window, fa_dtype_t dt) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lkv < 1) return FA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+    if (Lq >= kMaxLen || Lkv >= kMaxLen) return FA_ERR_SHAPE;
+    fa_status_t st = check_headdim(D, dt);
+    if (st != FA_OK) return st;
+    if ((long long)B * Hq * Lq * D > kMaxElems || (long long)B * Hkv * Lkv * D > kMaxElems) return FA_ERR_SHAPE;
+    if (window < 0 || !std::isfinite(scale)) return FA_ERR_ARG;
+    return FA_OK;
+}
+
+fa_status_t from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+// A window of Lq or more keys never masks anything (i - j <= Lq - 1 for every
+// pair), so it is the same as no window; folding it to 0 also keeps the
+// kernels' tile-range arithmetic far from int overflow.
+int effective_window(int window, int Lq) { return window >= Lq ? 0 : window; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status_t s) {
+    switch (s) {
+        case FA_OK: return "ok";
+        case FA_ERR_NULL: return "a required pointer is NULL";
+        case FA_ERR_SHAPE: return "bad shape: sizes must be >= 1, Hq a multiple of Hkv, within the size limits";
+        case FA_ERR_HEADDIM: return "head dim must be a multiple of 8 in [32, 512] ([32, 256] for FA_F32)";
+        case FA_ERR_DTYPE: return "unsupported dtype (FA_F32, FA_F16 or FA_BF16)";
+        case FA_ERR_ALIGN: return "every pointer must be 16-byte aligned";
+        case FA_ERR_ARG: return "window must be >= 0 and scale finite";
+        case FA_ERR_LAUNCH: return "HIP kernel launch failed";
+    }
+    return "unknown status";
+}
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                   int Lq, int Lkv, int D, float scale, int causal, int window, fa_dtype_t dtype, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    fa_status_t st = check_dtype(dtype);
+    if (st != FA_OK) return st;
+    st = check_attn(B, Hq, Hkv, Lq, Lkv, D, scale, window, dtype);
+    if (st != FA_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+
+    fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Lq, Lkv, D,
+                  (float)((double)scale * 1.4426950408889634), causal ? 1 : 0, effective_window(window, Lq)};
+    const int dmax = fa::dmax_bucket(D);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    switch (dtype) {
+        case FA_F32: return from_hip(fa::launch_fwd_f32(dmax, a, s));
+        case FA_F16: return from_hip(fa::launch_fwd_f16(dmax, a, s));
+        case FA_BF16: return from_hip(fa::launch_fwd_bf16(dmax, a, s));
+    }
+    return FA_ERR_DTYPE;
+}
+
+fa_status_t fa_bwd_preprocess(const void* o, const void* dO, float* delta, int B, int Hq, int Lq, int D,
+                              fa_dtype_t dtype, void* stream) {
+    if (!o || !dO || !delta) return FA_ERR_NULL;
+    fa_status_t st = check_dtype(dtype);
+    if (st != FA_OK) return st;
+    if (B < 1 || Hq < 1 || Lq < 1 || Lq >= kMaxLen) return FA_ERR_SHAPE;
+    st = check_headdim(D, dtype);
+    if (st != FA_OK) return st;
+    if ((long long)B * Hq * Lq * D > kMaxElems) return FA_ERR_SHAPE;
+    if (!aligned16(o) || !aligned16(dO) || !aligned16(delta)) return FA_ERR_ALIGN;
+
+    fa::PreArgs a{o, dO, delta, (long long)B * Hq * Lq, D};
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    switch (dtype) {
+        case FA_F32: return from_hip(fa::launch_pre_f32(a, s));
+        case FA_F16: return from_hip(fa::launch_pre_f16(a, s));
+        case FA_BF16: return from_hip(fa::launch_pre_bf16(a, s));
+    }
+    return FA_ERR_DTYPE;
+}
+
+static fa_status_t bwd_common(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                              const float* delta, int B, int Hq, int Hkv, int Lq, int Lkv, int D, float scale,
+                              int window, fa_dtype_t dtype) {
+    if (!q || !k || !v || !dO || !lse || !delta) return FA_ERR_NULL;
+    fa_status_t st = check_dtype(dtype);
+    if (st != FA_OK) return st;
+    st = check_attn(B, Hq, Hkv, Lq, Lkv, D, scale, window, dtype);
+    if (st != FA_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(lse) || !aligned16(delta))
+        return FA_ERR_ALIGN;
+    return FA_OK;
+}
+
+fa_status_t fa_bwd_dkv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                       const float* delta, void* dk, void* dv, int B, int Hq, int Hkv, int Lq, int Lkv, int D,
+                       float scale, int causal, int window, fa_dtype_t dtype, void* stream) {
+    if (!dk || !dv) return FA_ERR_NULL;
+    fa_status_t st = bwd_common(q, k, v, dO, lse, delta, B, Hq, Hkv, Lq, Lkv, D, scale, window, dtype);
+    if (st != FA_OK) return st;
+    if (!aligned16(dk) || !aligned16(dv)) return FA_ERR_ALIGN;
+
+    fa::BwdArgs a{q, k, v, dO, lse, delta, nullptr, dk, dv, B, Hq, Hkv, Lq, Lkv, D,
+                  (float)((double)scale * 1.4426950408889634), scale, causal ? 1 : 0,
+                  effective_window(window, Lq)};
+    const int dmax = fa::dmax_bucket(D);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    switch (dtype) {
+        case FA_F32: return from_hip(fa::launch_dkv_f32(dmax, a, s));
+        case FA_F16: return from_hip(fa::launch_dkv_f16(dmax, a, s));
+        case FA_BF16: return from_hip(fa::launch_dkv_bf16(dmax, a, s));
+    }
+    return FA_ERR_DTYPE;
+}
+
+fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                      const float* delta, void* dq, int B, int Hq, int Hkv, int Lq, int Lkv, int D, float scale,
+                      int causal, int window, fa_dtype_t dtype, void* stream) {
+    if (!dq) return FA_ERR_NULL;
+    fa_status_t st = bwd_common(q, k, v, dO, lse, delta, B, Hq, Hkv, Lq, Lkv, D, scale, window, dtype);
+    if (st != FA_OK) return st;
+    if (!aligned16(dq)) return FA_ERR_ALIGN;
+
+    fa::BwdArgs a{q, k, v, dO, lse, delta, dq, nullptr, nullptr, B, Hq, Hkv, Lq, Lkv, D,
+                  (float)((double)scale * 1.4426950408889634), scale, causal ? 1 : 0,
+                  effective_window(window, Lq)};
+    const int dmax = fa::dmax_bucket(D);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    switch (dtype) {
+        case FA_F32: return from_hip(fa::launch_dq_f32(dmax, a, s));
+        case FA_F16: return from_hip(fa::launch_dq_f16(dmax, a, s));
+        case FA_BF16: return from_hip(fa::launch_dq_bf16(dmax, a, s));
+    }
+    return FA_ERR_DTYPE;
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Kernel argument blocks and per-dtype launcher declarations shared by the
+// C-ABI front end (fa_api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace fa {
+
+// Forward: O = softmax(scale * Q K^T + mask) V and the natural-log LSE per row.
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int B, Hq, Hkv, Lq, Lkv, D;
+    float c;      // scale * log2(e): scores are handled in the exp2 domain
+    int causal;
+    int window;
+};
+
+// Backward pre-pass: delta = rowsum(dO * O) over rows of length D.
+struct PreArgs {
+    const void* o;
+    const void* dO;
+    float* delta;
+    long long rows;
+    int D;
+};
+
+// dK/dV and dQ kernels.
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dO;
+    const float* lse;
+    const float* delta;
+    void* dq;
+    void* dk;
+    void* dv;
+    int B, Hq, Hkv, Lq, Lkv, D;
+    float c;      // scale * log2(e)
+    float scale;  // applied once to dQ and dK in the epilogue
+    int causal;
+    int window;
+};
+
+// Element-type tags understood by the launchers.
+enum class Ty { F32 = 0, F16 = 1, BF16 = 2 };
+
+// Head-dim buckets: a runtime D is served by the smallest bucket >= D, with
+// the columns past D zero-filled on load and never stored.
+inline int dmax_bucket(int D) {
+    if (D <= 32) return 32;
+    if (D <= 64) return 64;
+    if (D <= 96) return 96;
+    if (D <= 128) return 128;
+    if (D <= 256) return 256;
+    return 512;
+}
+
+hipError_t launch_fwd_f32(int dmax, const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_f16(int dmax, const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_bf16(int dmax, const FwdArgs& a, hipStream_t s);
+hipError_t launch_pre_f32(const PreArgs& a, hipStream_t s);
+hipError_t launch_pre_f16(const PreArgs& a, hipStream_t s);
+hipError_t launch_pre_bf16(const PreArgs& a, hipStream_t s);
+hipError_t launch_dkv_f32(int dmax, const BwdArgs& a, hipStream_t s);
+hipError_t launch_dkv_f16(int dmax, const BwdArgs& a, hipStream_t s);
+hipError_t launch_dkv_bf16(int dmax, const BwdArgs& a, hipStream_t s);
+hipError_t launch_dq_f32(int dmax, const BwdArgs& a, hipStream_t s);
+hipError_t launch_dq_f16(int dmax, const BwdArgs& a, hipStream_t s);
+hipError_t launch_dq_bf16(int dmax, const BwdArgs& a, hipStream_t s);
+
+}  // namespace fa

@@ -1,0 +1,259 @@
+"""Benchmark: fwd+bwd attention TFLOP/s and % of bf16 dense MFMA peak on one MI355X.
+
+One step = fa_fwd -> fa_bwd_preprocess -> fa_bwd_dkv -> fa_bwd_dq on inputs
+already resident in HBM (the whole hot path, through the C ABI). W untimed
+warm-up steps, then K timed steps bracketed by synchronisation; HIP events on
+the stream the kernels are launched on give the step time and, in a second
+timed pass, each kernel's average duration.
+
+FLOP count (algorithmic): N = allowed (i, j) pairs per (batch, head), exactly
+counted from the mask; forward = 4*D*N*B*Hq, backward = 2.5 x forward.
+The "formula" count halves the dense count under causal masking and ignores
+the window.
+
+Prints ONE JSON line. --gpus N > 1 exits: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+METRIC = "fwd+bwd attention TFLOP/s and % of bf16 MFMA peak (1 GPU)"
+
+
+def allowed_pairs(Lq: int, Lkv: int, causal: bool, window: int) -> int:
+    """Exact count of allowed (i, j) pairs under the mask rule."""
+    total = 0
+    for i in range(Lq):
+        hi = min(i, Lkv - 1) if causal else Lkv - 1
+        lo = max(0, i - window + 1) if window else 0
+        if causal or not window:
+            total += max(0, hi - lo + 1)
+        else:  # window without causal: past trimmed, all future keys kept
+            total += max(0, Lkv - lo)
+    return total
+
+
+def workload_flops(w):
+    n = allowed_pairs(w.Lq, w.Lkv, w.causal, w.window)
+    fwd = 4.0 * w.D * n * w.B * w.Hq
+    dense = 4.0 * w.D * w.Lq * w.Lkv * w.B * w.Hq * (0.5 if w.causal else 1.0)
+    return {"pairs": n, "fwd": fwd, "bwd": 2.5 * fwd, "total": 3.5 * fwd, "formula_total": 3.5 * dense,
+            # per-kernel work actually required by each kernel's own outputs:
+            # dK/dV: S, dP, dV, dK = 4 contractions; dQ: S, dP, dQ = 3
+            "dkv": 8.0 * w.D * n * w.B * w.Hq, "dq": 6.0 * w.D * n * w.B * w.Hq}
+
+
+def workload_bytes(w):
+    e = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
+    q = w.B * w.Hq * w.Lq * w.D * e
+    kv = w.B * w.Hkv * w.Lkv * w.D * e
+    row = w.B * w.Hq * w.Lq * 4
+    return {"fwd": 2 * q + 2 * kv + row, "pre": 2 * q + row, "dkv": 2 * q + 4 * kv + 2 * row,
+            "dq": 3 * q + 2 * kv + 2 * row}
+
+
+def time_gpu(w, steps: int, warmup: int):
+    import torch
+
+    import attention_fa_fwd_06_amd as fa
+    from synth import to_torch, workload_inputs
+
+    fa.load_library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    x = workload_inputs(w)
+    q, k, v, do = (to_torch(x[n], w.dtype).to(dev) for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    lse = torch.empty((w.B, w.Hq, w.Lq), device=dev, dtype=torch.float32)
+    delta = torch.empty_like(lse)
+    sc, ca, wi = w.scale, w.causal, w.window
+
+    kernels = [
+        ("fa_fwd", lambda: fa.fa_fwd(q, k, v, o, lse, sc, ca, wi)),
+        ("fa_bwd_preprocess", lambda: fa.fa_bwd_preprocess(o, do, delta)),
+        ("fa_bwd_dkv", lambda: fa.fa_bwd_dkv(q, k, v, do, lse, delta, dk, dv, sc, ca, wi)),
+        ("fa_bwd_dq", lambda: fa.fa_bwd_dq(q, k, v, do, lse, delta, dq, sc, ca, wi)),
+    ]
+
+    def step():
+        for _, f in kernels:
+            f()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / steps
+
+    # second pass: per-kernel durations, events around every launch
+    ev = {name: [] for name, _ in kernels}
+    for _ in range(steps):
+        for name, f in kernels:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            f()
+            b.record(stream)
+            ev[name].append((a, b))
+    torch.cuda.synchronize()
+    per = {name: sum(a.elapsed_time(b) for a, b in pairs) / len(pairs) for name, pairs in ev.items()}
+    return ms_step, wall * 1e3 / steps, per
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """The float64 oracle on a bounded sample of the workload: whole (batch,
+    kv-group) slices, run until about budget_s seconds have been spent."""
+    import numpy as np
+
+    import oracle
+    from synth import decode, workload_inputs
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    x = workload_inputs(w)
+    reps = w.Hq // w.Hkv
+    done, flops, t_total = 0, 0.0, 0.0
+    groups = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+    per_head = workload_flops(w)["total"] / (w.B * w.Hq)
+    for b, g in groups:
+        hs = slice(g * reps, (g + 1) * reps)
+        args = [decode(x["q"][b:b + 1, hs], w.dtype), decode(x["k"][b:b + 1, g:g + 1], w.dtype),
+                decode(x["v"][b:b + 1, g:g + 1], w.dtype), decode(x["do"][b:b + 1, hs], w.dtype)]
+        t = time.perf_counter()
+        oracle.backward(*args, w.scale, w.causal, w.window)
+        t_total += time.perf_counter() - t
+        done += 1
+        flops += per_head * reps
+        if t_total >= budget_s:
+            break
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {len(groups)} (batch, kv-group) slices ({done * reps} of {w.B * w.Hq} query heads), "
+                      f"full fwd+bwd in float64, {t_total:.2f} s",
+            "seconds": t_total}
+
+
+def run(w, steps, warmup, with_cpu):
+    f = workload_flops(w)
+    by = workload_bytes(w)
+    ms, wall_ms, per = time_gpu(w, steps, warmup)
+    tflops = f["total"] / (ms * 1e-3) / 1e12
+    peak = PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+    res = {
+        "workload": w,
+        "ms_per_step": ms,
+        "wall_ms_per_step": wall_ms,
+        "tflops": tflops,
+        "tflops_formula": f["formula_total"] / (ms * 1e-3) / 1e12,
+        "pct_peak": 100.0 * tflops / peak,
+        "per_kernel_ms": per,
+        "fwd_ms": per["fa_fwd"],
+        "bwd_ms": per["fa_bwd_preprocess"] + per["fa_bwd_dkv"] + per["fa_bwd_dq"],
+        "flops": f,
+        "bytes": by,
+    }
+    dom = max(("fa_fwd", "fa_bwd_dkv", "fa_bwd_dq"), key=lambda n: per[n])
+    unit_flops = {"fa_fwd": f["fwd"], "fa_bwd_dkv": f["dkv"], "fa_bwd_dq": f["dq"]}[dom]
+    achieved = unit_flops / (per[dom] * 1e-3) / 1e12
+    res["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                       "frac": achieved / peak, "traffic": None, "avg_ms": per[dom]}
+    res["kernel_tflops"] = {n: unit_flops_n / (per[n] * 1e-3) / 1e12 for n, unit_flops_n in
+                            (("fa_fwd", f["fwd"]), ("fa_bwd_dkv", f["dkv"]), ("fa_bwd_dq", f["dq"]))}
+    res["pre_gbs"] = by["pre"] / (per["fa_bwd_preprocess"] * 1e-3) / 1e9
+    if with_cpu:
+        res["cpu_baseline"] = cpu_baseline(w)
+    return res
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, help="index into synth.WORKLOADS (default: the 2048-token GQA)")
+    ap.add_argument("--also", type=str, default="3", help="comma list of extra workload indices reported inline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this attention path runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    from synth import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    main_res = run(w, args.steps, args.warmup, not args.no_cpu_baseline)
+    extra = {}
+    for idx in [int(s) for s in args.also.split(",") if s.strip() != ""]:
+        if idx == args.workload:
+            continue
+        r = run(WORKLOADS[idx], args.steps, args.warmup, False)
+        extra[WORKLOADS[idx].name] = {
+            "ms_per_step": round(r["ms_per_step"], 4), "tflops": round(r["tflops"], 2),
+            "tflops_formula": round(r["tflops_formula"], 2), "pct_peak": round(r["pct_peak"], 2),
+            "per_kernel_ms": {k: round(v, 4) for k, v in r["per_kernel_ms"].items()},
+            "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r["roofline"].items()},
+        }
+
+    r = main_res
+    line = {
+        "metric": METRIC,
+        "value": round(r["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, the workload's shapes)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Lq": w.Lq, "Lkv": w.Lkv, "D": w.D,
+                   "causal": w.causal, "window": w.window, "parallelism": "single GPU"},
+        "pct_of_bf16_peak": round(r["pct_peak"], 3),
+        "tflops_formula_count": round(r["tflops_formula"], 3),
+        "fwd_ms": round(r["fwd_ms"], 4),
+        "bwd_ms": round(r["bwd_ms"], 4),
+        "per_kernel_ms": {k: round(v, 4) for k, v in r["per_kernel_ms"].items()},
+        "kernel_tflops": {k: round(v, 2) for k, v in r["kernel_tflops"].items()},
+        "preprocess_gbs": round(r["pre_gbs"], 1),
+        "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r["roofline"].items()},
+        "cpu_baseline": r.get("cpu_baseline"),
+        "also": extra,
+    }
+    if line["cpu_baseline"] is not None:
+        cb = dict(line["cpu_baseline"])
+        cb["value"] = float(f"{cb['value']:.4g}")
+        cb["seconds"] = round(cb["seconds"], 2)
+        line["cpu_baseline"] = cb
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

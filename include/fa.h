@@ -1,0 +1,129 @@
+/*
+ * fa.h — C ABI of the MI355X (gfx950) FlashAttention-2 training attention.
+ *
+ * Four calls make one training step of softmax attention:
+ *   fa_fwd            O = softmax(scale * Q K^T + mask) V, plus the per-row LSE
+ *   fa_bwd_preprocess Delta = rowsum(dO * O)
+ *   fa_bwd_dkv        dK, dV (each workgroup owns a block of K/V rows; no atomics)
+ *   fa_bwd_dq         dQ
+ *
+ * Sources: mlx-bun flash-attention.ts (flashForward and flashBackward host
+ * functions and the forward, D pre-pass, dK/dV and dQ shaders); the MLX pull
+ * request "[Metal] Add Flash Attention VJP for training" (implementation notes:
+ * LSE cached by the forward, two-kernel atomics-free backward with K-row
+ * ownership); ggmlR R/ag_flash_attn.R (ag_flash_attention: argument checks that
+ * raise errors instead of aborting, default scale 1/sqrt(d_head)).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Layout: row-major, head_dim fastest, contiguous.
+ *   q, o, dO, dQ : [B, Hq,  Lq,  D]
+ *   k, v, dK, dV : [B, Hkv, Lkv, D]
+ *   lse, delta   : [B, Hq,  Lq]  always float32
+ * q, k, v, o, dO, dQ, dK and dV share one element type (fa_dtype_t); all
+ * accumulation is float32.
+ * GQA/MQA: Hq must be a multiple of Hkv; query head h reads kv head h / (Hq/Hkv),
+ * so consecutive query heads share a kv head.
+ * Mask: query row i may attend key j iff
+ *   (!causal || j <= i) && (window == 0 || j > i || i - j < window).
+ * Causal is aligned top-left (row i sees keys 0..i) also when Lq != Lkv. A
+ * window keeps the query's own key and the window-1 keys before it; without
+ * causal it trims only the past. window == 0 disables it.
+ * scale multiplies Q K^T before masking and before the LSE; the usual value is
+ * 1/sqrt(D).
+ * lse is the NATURAL-log logsumexp of the scaled, masked scores of each row.
+ * A row with no allowed key gets O = 0, lse = -inf and no gradient.
+ *
+ * Ownership and execution
+ * -----------------------
+ * Every pointer is a DEVICE pointer owned by the caller; the library allocates,
+ * frees and synchronises nothing and keeps no state. All work is enqueued on
+ * `stream` (a hipStream_t; NULL = the null stream) and the call returns right
+ * after the launch. Outputs must not alias inputs. Required order on one
+ * stream: fa_fwd -> fa_bwd_preprocess -> {fa_bwd_dkv, fa_bwd_dq} (the last two
+ * are independent of each other). Results are deterministic: the same inputs
+ * give bit-identical outputs.
+ *
+ * Errors
+ * ------
+ * Arguments are checked before anything is launched; a bad argument returns a
+ * negative fa_status_t and touches no memory. The library never aborts.
+ * FA_ERR_LAUNCH reports a failure of the HIP launch itself.
+ *
+ * Limits: 1 <= B, Hq, Hkv, Lq, Lkv; Hq % Hkv == 0; 32 <= D <= 512 and
+ * D % 8 == 0 (D <= 256 for FA_F32); window >= 0; scale finite; every pointer 16-byte aligned;
+ * B*Hq*Lq*D and B*Hkv*Lkv*D below 2^31; Lq, Lkv below 2^24.
+ */
+#ifndef FA_H
+#define FA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_F32 = 0,
+    FA_F16 = 1,
+    FA_BF16 = 2
+} fa_dtype_t;
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = -1,    /* a required pointer is NULL */
+    FA_ERR_SHAPE = -2,   /* a size is < 1, too large, or Hq % Hkv != 0 */
+    FA_ERR_HEADDIM = -3, /* D outside [32, 512] ([32, 256] for FA_F32) or not a multiple of 8 */
+    FA_ERR_DTYPE = -4,   /* dtype is not one of fa_dtype_t */
+    FA_ERR_ALIGN = -5,   /* a pointer is not 16-byte aligned */
+    FA_ERR_ARG = -6,     /* negative window or non-finite scale */
+    FA_ERR_LAUNCH = -7   /* the HIP kernel launch failed */
+} fa_status_t;
+
+/*
+ * Forward (mlx-bun flash-attention.ts, flashForward and the forward shader).
+ * Reads q, k, v; writes o [B,Hq,Lq,D] (dtype) and lse [B,Hq,Lq] (float32).
+ */
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int Lq, int Lkv, int D,
+                   float scale, int causal, int window, fa_dtype_t dtype, void* stream);
+
+/*
+ * Backward pre-pass (mlx-bun flash-attention.ts, D pre-pass shader):
+ * delta[b,h,i] = sum_d dO[b,h,i,d] * o[b,h,i,d] in float32, from the stored o.
+ * Reads o and dO [B,Hq,Lq,D]; writes delta [B,Hq,Lq] (float32).
+ */
+fa_status_t fa_bwd_preprocess(const void* o, const void* dO, float* delta,
+                              int B, int Hq, int Lq, int D, fa_dtype_t dtype, void* stream);
+
+/*
+ * dK and dV (mlx-bun flash-attention.ts, dK/dV shader; MLX VJP pull request,
+ * K-row ownership). Each workgroup owns a block of K/V rows of one kv head and
+ * loops over every query tile of every query head in its group, so dK and dV
+ * are written once, without atomics:
+ *   P  = exp(scale * Q K^T - lse)   (0 where masked)
+ *   dS = P * (dO V^T - delta)
+ *   dV = sum_h P^T dO,   dK = scale * sum_h dS^T Q.
+ * Reads q, k, v, dO, lse, delta; writes dk, dv [B,Hkv,Lkv,D] (dtype).
+ */
+fa_status_t fa_bwd_dkv(const void* q, const void* k, const void* v, const void* dO,
+                       const float* lse, const float* delta, void* dk, void* dv,
+                       int B, int Hq, int Hkv, int Lq, int Lkv, int D,
+                       float scale, int causal, int window, fa_dtype_t dtype, void* stream);
+
+/*
+ * dQ (mlx-bun flash-attention.ts, dQ shader; MLX VJP pull request, dQ kernel
+ * with an outer loop over KV blocks): dQ = scale * dS K with dS as above.
+ * Reads q, k, v, dO, lse, delta; writes dq [B,Hq,Lq,D] (dtype).
+ */
+fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
+                      const float* lse, const float* delta, void* dq,
+                      int B, int Hq, int Hkv, int Lq, int Lkv, int D,
+                      float scale, int causal, int window, fa_dtype_t dtype, void* stream);
+
+/* Static, never-NULL description of a status code. */
+const char* fa_status_string(fa_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -4,6 +4,7 @@ from .attention import (  # noqa: F401
     backward,
     bwd_preprocess,
     forward,
+    key_span,
     mask_matrix,
     rows_forward,
     sample_keys,

@@ -76,15 +76,24 @@ def _kv_head(h: int, Hq: int, Hkv: int) -> int:
     return h // (Hq // Hkv)
 
 
-def rows_forward(q_rows, K, V, rows, scale, causal, window):
+def rows_forward(q_rows, K, V, rows, scale, causal, window, cols=None):
     """Forward for a set of query rows of one (b, h).
 
     q_rows [R, D], K and V [Lkv, D], rows = the R absolute row indices.
+    cols (optional) = absolute key indices to evaluate; it must contain every
+    allowed key of every row, and then the result is exact, because masked
+    probabilities are exactly 0 (the returned S and P cover only cols).
     Returns S (masked, -inf where forbidden), P, O [R, D], LSE [R].
     """
     q_rows = np.asarray(q_rows, dtype=np.float64)
-    S = scale * (q_rows @ K.T)
-    ok = mask_matrix(rows, K.shape[0], causal, window)
+    if cols is None:
+        cols = np.arange(K.shape[0])
+        Kc, Vc = K, V
+    else:
+        cols = np.asarray(cols)
+        Kc, Vc = K[cols], V[cols]
+    S = scale * (q_rows @ Kc.T)
+    ok = mask_matrix(rows, K.shape[0], causal, window, cols=cols)
     S = np.where(ok, S, -np.inf)
     m = S.max(axis=1)
     live = np.isfinite(m)
@@ -95,8 +104,17 @@ def rows_forward(q_rows, K, V, rows, scale, causal, window):
     lse0 = np.where(live, lse, 0.0)
     with np.errstate(under="ignore"):
         P = np.where(ok & live[:, None], np.exp(S - lse0[:, None]), 0.0)
-    O = P @ V
+    O = P @ Vc
     return S, P, O, lse
+
+
+def key_span(rows, Lkv, causal, window):
+    """Smallest contiguous key range [lo, hi] holding every allowed key of the rows
+    (from the mask rule: causal caps keys at the row, a window floors them)."""
+    rows = np.asarray(rows)
+    lo = max(0, int(rows.min()) - window + 1) if window else 0
+    hi = min(Lkv - 1, int(rows.max())) if causal else Lkv - 1
+    return np.arange(lo, hi + 1) if hi >= lo else np.arange(0)
 
 
 def forward(q, k, v, scale, causal=False, window=0):
@@ -155,42 +173,53 @@ def backward(q, k, v, do, scale, causal=False, window=0):
 # ---------------------------------------------------------------------------
 
 def sample_rows(q, k, v, do, scale, causal, window, b, h, rows):
-    """O, LSE, Delta, dQ for the given query rows of (b, h)."""
-    Hq, Hkv = q.shape[1], k.shape[1]
+    """O, LSE, Delta, dQ for the given query rows of (b, h), one row at a time
+    over that row's allowed key span."""
+    Hq, Hkv, Lkv = q.shape[1], k.shape[1], k.shape[2]
     g = _kv_head(h, Hq, Hkv)
     Kg, Vg = k[b, g], v[b, g]
-    rows = np.asarray(rows)
-    _, P, O, lse = rows_forward(q[b, h, rows], Kg, Vg, rows, scale, causal, window)
-    dOr = do[b, h, rows]
-    delta = bwd_preprocess(O, dOr)
-    dS = P * (dOr @ Vg.T - delta[:, None])
-    return {"O": O, "LSE": lse, "Delta": delta, "dQ": scale * (dS @ Kg)}
+    out = {"O": [], "LSE": [], "Delta": [], "dQ": []}
+    for i in np.asarray(rows):
+        cols = key_span([i], Lkv, causal, window)
+        if len(cols) == 0:
+            cols = np.arange(1)  # every key masked: a single masked column gives O = 0, LSE = -inf
+        _, P, O, lse = rows_forward(q[b, h, [i]], Kg, Vg, [i], scale, causal, window, cols)
+        dOr = do[b, h, [i]]
+        delta = bwd_preprocess(O, dOr)
+        dS = P * (dOr @ Vg[cols].T - delta[:, None])
+        out["O"].append(O[0])
+        out["LSE"].append(lse[0])
+        out["Delta"].append(delta[0])
+        out["dQ"].append(scale * (dS @ Kg[cols])[0])
+    return {key: np.array(val) for key, val in out.items()}
 
 
 def sample_keys(q, k, v, do, scale, causal, window, b, g, keys):
-    """dK, dV for the given keys of kv head g in batch b.
+    """dK, dV for the given keys of kv head g in batch b, one key at a time.
 
-    Every query row that may attend one of the keys contributes, for every
-    query head of the group; each such row's LSE and Delta come from its own
-    full row of scores.
+    Every query row that may attend the key contributes, for every query head
+    of the group; each such row's LSE and Delta come from its own scores over
+    the key span that holds all of that row's allowed keys.
     """
     Hq, Hkv = q.shape[1], k.shape[1]
     Lq, Lkv = q.shape[2], k.shape[2]
     reps = Hq // Hkv
-    keys = np.asarray(keys)
     Kg, Vg = k[b, g], v[b, g]
-    any_ok = mask_matrix(np.arange(Lq), Lkv, causal, window, cols=keys).any(axis=1)
-    rows = np.nonzero(any_ok)[0]
+    keys = np.asarray(keys)
     dK = np.zeros((len(keys), Kg.shape[1]))
     dV = np.zeros((len(keys), Vg.shape[1]))
-    if len(rows) == 0:
-        return {"dK": dK, "dV": dV}
-    for r in range(reps):
-        h = g * reps + r
-        _, P, O, lse = rows_forward(q[b, h, rows], Kg, Vg, rows, scale, causal, window)
-        dOr = do[b, h, rows]
-        delta = bwd_preprocess(O, dOr)
-        dS = P * (dOr @ Vg.T - delta[:, None])
-        dK += scale * (dS[:, keys].T @ q[b, h, rows])
-        dV += P[:, keys].T @ dOr
+    for n, j in enumerate(keys):
+        rows = np.nonzero(mask_matrix(np.arange(Lq), Lkv, causal, window, cols=[j])[:, 0])[0]
+        if len(rows) == 0:
+            continue
+        cols = key_span(rows, Lkv, causal, window)
+        jc = int(np.nonzero(cols == j)[0][0])
+        for r in range(reps):
+            h = g * reps + r
+            _, P, O, _ = rows_forward(q[b, h, rows], Kg, Vg, rows, scale, causal, window, cols)
+            dOr = do[b, h, rows]
+            delta = bwd_preprocess(O, dOr)
+            dS = P * (dOr @ Vg[cols].T - delta[:, None])
+            dK[n] += scale * (dS[:, jc] @ q[b, h, rows])
+            dV[n] += P[:, jc] @ dOr
     return {"dK": dK, "dV": dV}

@@ -1,0 +1,31 @@
+"""Host-side logic of bench.py (no GPU): exact allowed-pair counts."""
+import numpy as np
+import pytest
+
+import bench
+import oracle
+from synth import WORKLOADS
+
+
+@pytest.mark.parametrize("Lq,Lkv,causal,window", [(7, 7, False, 0), (9, 9, True, 0), (12, 12, True, 4),
+                                                  (10, 6, True, 3), (6, 10, False, 2), (5, 9, True, 0),
+                                                  (30, 30, False, 7)])
+def test_allowed_pairs_matches_mask(Lq, Lkv, causal, window):
+    want = int(oracle.mask_matrix(np.arange(Lq), Lkv, causal, window).sum())
+    assert bench.allowed_pairs(Lq, Lkv, causal, window) == want
+
+
+def test_workload_pair_counts():
+    # closed forms: causal L(L+1)/2; causal + window W(W+1)/2 + (L-W)W
+    assert bench.allowed_pairs(2048, 2048, True, 0) == 2048 * 2049 // 2 == 2098176
+    assert bench.allowed_pairs(8192, 8192, True, 1024) == 1024 * 1025 // 2 + (8192 - 1024) * 1024 == 7864832
+    assert bench.allowed_pairs(32768, 32768, True, 0) == 536887296
+    f = bench.workload_flops(WORKLOADS[2])
+    assert abs(f["total"] - 4.813e11) / 4.813e11 < 1e-3
+
+
+def test_gpus_other_than_one_exit(capsys):
+    with pytest.raises(SystemExit) as e:
+        bench.main(["--gpus", "2"])
+    assert e.value.code == 2
+    assert "one GPU" in capsys.readouterr().out

@@ -1,0 +1,169 @@
+"""C-ABI boundary checks that need no GPU.
+
+Every call here either only loads the library or passes an argument that the
+library must reject before it makes any HIP call; none of them launches work.
+The fake device pointers are never dereferenced.
+"""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import attention_fa_fwd_06_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+OK, NULL, SHAPE, HEADDIM, DTYPE, ALIGN, ARG = 0, -1, -2, -3, -4, -5, -6
+P = 0x10000  # 16-byte aligned, never dereferenced
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.fail("libfa.so is not built: run python -m attention_fa_fwd_06_amd.build")
+    return fa.load_library()
+
+
+def test_header_declares_the_four_calls():
+    assert _declared() == sorted(fa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    for name in _declared():
+        assert name in exported, name
+
+
+def test_status_strings(lib):
+    for code in range(-7, 1):
+        s = fa.status_string(code)
+        assert isinstance(s, str) and s
+    assert fa.status_string(0) == "ok"
+    assert fa.status_string(-99) == "unknown status"
+
+
+def _fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=4, Hkv=2, Lq=64, Lkv=64, D=64, scale=0.125, causal=1, window=0,
+         dtype=fa.FA_BF16):
+    return lib.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Lq, Lkv, D, scale, causal, window, dtype, None)
+
+
+def _dkv(lib, ptrs=(P,) * 8, B=1, Hq=4, Hkv=2, Lq=64, Lkv=64, D=64, scale=0.125, causal=1, window=0,
+         dtype=fa.FA_BF16):
+    return lib.fa_bwd_dkv(*ptrs, B, Hq, Hkv, Lq, Lkv, D, scale, causal, window, dtype, None)
+
+
+def _dq(lib, ptrs=(P,) * 7, B=1, Hq=4, Hkv=2, Lq=64, Lkv=64, D=64, scale=0.125, causal=1, window=0,
+        dtype=fa.FA_BF16):
+    return lib.fa_bwd_dq(*ptrs, B, Hq, Hkv, Lq, Lkv, D, scale, causal, window, dtype, None)
+
+
+@pytest.mark.parametrize("which", range(5))
+def test_fwd_null_pointers(lib, which):
+    args = dict(q=P, k=P, v=P, o=P, lse=P)
+    args[list(args)[which]] = None
+    assert _fwd(lib, **args) == NULL
+
+
+@pytest.mark.parametrize("which", range(8))
+def test_dkv_null_pointers(lib, which):
+    ptrs = [P] * 8
+    ptrs[which] = None
+    assert _dkv(lib, ptrs) == NULL
+
+
+@pytest.mark.parametrize("which", range(7))
+def test_dq_null_pointers(lib, which):
+    ptrs = [P] * 7
+    ptrs[which] = None
+    assert _dq(lib, ptrs) == NULL
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(B=0), SHAPE),
+        (dict(Hq=0), SHAPE),
+        (dict(Hkv=0), SHAPE),
+        (dict(Lq=0), SHAPE),
+        (dict(Lkv=0), SHAPE),
+        (dict(Hq=6, Hkv=4), SHAPE),
+        (dict(Lq=1 << 24), SHAPE),
+        (dict(B=1 << 12, Hq=64, Hkv=64, Lq=1 << 12, Lkv=16, D=128), SHAPE),
+        (dict(D=24), HEADDIM),
+        (dict(D=36), HEADDIM),
+        (dict(D=520), HEADDIM),
+        (dict(D=264, dtype=fa.FA_F32), HEADDIM),
+        (dict(D=512, dtype=fa.FA_F32), HEADDIM),
+        (dict(dtype=3), DTYPE),
+        (dict(dtype=-1), DTYPE),
+        (dict(window=-1), ARG),
+        (dict(scale=math.inf), ARG),
+        (dict(scale=math.nan), ARG),
+    ],
+)
+def test_bad_arguments_are_rejected_by_all_attention_calls(lib, kw, code):
+    assert _fwd(lib, **kw) == code
+    assert _dkv(lib, **kw) == code
+    assert _dq(lib, **kw) == code
+
+
+@pytest.mark.parametrize("which", range(5))
+def test_fwd_misaligned_pointer(lib, which):
+    args = dict(q=P, k=P, v=P, o=P, lse=P)
+    args[list(args)[which]] = P + 8
+    assert _fwd(lib, **args) == ALIGN
+
+
+@pytest.mark.parametrize("which", range(8))
+def test_dkv_misaligned_pointer(lib, which):
+    ptrs = [P] * 8
+    ptrs[which] = P + 4
+    assert _dkv(lib, ptrs) == ALIGN
+
+
+def test_preprocess_rejections(lib):
+    f = lib.fa_bwd_preprocess
+    assert f(None, P, P, 1, 2, 16, 64, fa.FA_F16, None) == NULL
+    assert f(P, None, P, 1, 2, 16, 64, fa.FA_F16, None) == NULL
+    assert f(P, P, None, 1, 2, 16, 64, fa.FA_F16, None) == NULL
+    assert f(P, P, P, 0, 2, 16, 64, fa.FA_F16, None) == SHAPE
+    assert f(P, P, P, 1, 2, 0, 64, fa.FA_F16, None) == SHAPE
+    assert f(P, P, P, 1, 2, 16, 60, fa.FA_F16, None) == HEADDIM
+    assert f(P, P, P, 1, 2, 16, 64, 7, None) == DTYPE
+    assert f(P + 2, P, P, 1, 2, 16, 64, fa.FA_F16, None) == ALIGN
+    assert f(P, P, P + 12, 1, 2, 16, 64, fa.FA_F16, None) == ALIGN
+
+
+def test_binding_rejects_cpu_tensors_before_calling(lib):
+    q = torch.zeros(1, 2, 16, 32)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, q[:, :1].contiguous(), q[:, :1].contiguous(), q.clone(), torch.zeros(1, 2, 16), 0.1)
+
+
+def test_binding_checks_shapes(lib):
+    q = torch.zeros(1, 2, 16, 32)
+    k = torch.zeros(1, 1, 16, 32)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, k, torch.zeros(1, 1, 8, 32), q.clone(), torch.zeros(1, 2, 16), 0.1)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, torch.zeros(1, 1, 16, 64), torch.zeros(1, 1, 16, 64), q.clone(), torch.zeros(1, 2, 16), 0.1)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(fa, "_lib", None)
+    with pytest.raises(RuntimeError):
+        fa.load_library(str(tmp_path / "nope.so"))

@@ -420,3 +420,29 @@ def test_planted_mistakes_are_caught(monkeypatch, mistake):
     elif mistake == "kv_head_modulo":
         monkeypatch.setattr(oa, "_kv_head", lambda h, Hq, Hkv: h % Hkv)
     assert not _pins_pass()
+
+
+def test_sampling_with_cross_lengths_and_empty_rows():
+    # Lq > Lkv with causal + window leaves rows with no allowed key at all
+    q, k, v, do = _case(B=1, Hq=4, Hkv=2, Lq=12, Lkv=5, D=4, seed=15)
+    for causal, window in [(True, 2), (True, 0), (False, 3)]:
+        r = oracle.backward(q, k, v, do, 0.5, causal, window)
+        rows = list(range(12))
+        s = oracle.sample_rows(q, k, v, do, 0.5, causal, window, 0, 1, rows)
+        for key in ("O", "Delta", "dQ"):
+            np.testing.assert_allclose(s[key], r[key][0, 1, rows], atol=1e-13)
+        assert np.array_equal(np.isneginf(s["LSE"]), np.isneginf(r["LSE"][0, 1]))
+        fin = np.isfinite(s["LSE"])
+        np.testing.assert_allclose(s["LSE"][fin], r["LSE"][0, 1][fin], atol=1e-13)
+        keys = list(range(5))
+        s = oracle.sample_keys(q, k, v, do, 0.5, causal, window, 0, 1, keys)
+        np.testing.assert_allclose(s["dK"], r["dK"][0, 1, keys], atol=1e-13)
+        np.testing.assert_allclose(s["dV"], r["dV"][0, 1, keys], atol=1e-13)
+
+
+def test_key_span_holds_every_allowed_key():
+    for Lq, Lkv, causal, window in [(9, 9, True, 3), (9, 4, True, 2), (6, 9, False, 2), (7, 7, False, 0)]:
+        ok = oracle.mask_matrix(np.arange(Lq), Lkv, causal, window)
+        for i in range(Lq):
+            span = oracle.key_span([i], Lkv, causal, window)
+            assert set(np.nonzero(ok[i])[0]) <= set(span.tolist())
