@@ -91,11 +91,12 @@ template <> struct Mma<_Float16> {
     }
 };
 template <> struct Mma<float> {
+    // The chunk is reinterpreted as a whole float vector before indexing: a
+    // bit cast of a single vector element subscript compiles to element 0.
     static __device__ __forceinline__ void nat(f32x16& acc, u32x4 a, u32x4 b) {
+        const f32x4 fa = __builtin_bit_cast(f32x4, a), fb = __builtin_bit_cast(f32x4, b);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a[i]),
-                                                       __builtin_bit_cast(float, b[i]), acc, 0, 0, 0);
+        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i], fb[i], acc, 0, 0, 0);
     }
 };
 
@@ -141,13 +142,11 @@ template <class T> struct MmaTr {
 };
 template <> struct MmaTr<float> {
     static __device__ __forceinline__ void run(f32x16& acc, const char* p, const PF<float>& pf) {
-        u32x4 a0 = ld16(p), a1 = ld16(p + 16);
+        const f32x4 a0 = __builtin_bit_cast(f32x4, ld16(p)), a1 = __builtin_bit_cast(f32x4, ld16(p + 16));
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a0[i]), pf.lo[i], acc, 0, 0, 0);
+        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0[i], pf.lo[i], acc, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a1[i]), pf.hi[i], acc, 0, 0, 0);
+        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[i], pf.hi[i], acc, 0, 0, 0);
     }
 };
 
