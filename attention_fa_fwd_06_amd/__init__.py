@@ -22,7 +22,8 @@ import math
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfa.so")
+# The in-tree build; FA_LIBRARY may name another build of the same sources.
+LIB_PATH = os.environ.get("FA_LIBRARY") or os.path.join(_HERE, "libfa.so")
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 STATUS = {

@@ -41,9 +41,9 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found: the ROCm toolchain is required to build libfa.so")
 
 
-def _compile(src: str, resource_usage: bool) -> tuple[str, str]:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, resource_usage: bool, build_dir: str, defines: list[str]) -> tuple[str, str]:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc(), *COMMON, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
     if resource_usage and src.endswith(".hip"):
         cmd.append("-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,38 +52,48 @@ def _compile(src: str, resource_usage: bool) -> tuple[str, str]:
     return obj, r.stderr
 
 
-def build(verbose: bool = False, resource_usage: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, resource_usage: bool = False, defines=(), out: str = LIB,
+          build_dir: str = BUILD) -> str:
+    """Compile every source and link `out` (default: the in-tree libfa.so).
+
+    defines: extra preprocessor definitions, e.g. tile overrides for sweeps.
+    """
+    defines = list(defines)
+    os.makedirs(build_dir, exist_ok=True)
     jobs = min(len(SOURCES), os.cpu_count() or 1)
     logs = []
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = [ex.submit(_compile, s, resource_usage) for s in SOURCES]
+        futs = [ex.submit(_compile, s, resource_usage, build_dir, defines) for s in SOURCES]
         objs = []
         for f in futs:
             obj, log = f.result()
             objs.append(obj)
             logs.append(log)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose or resource_usage:
         for log in logs:
             lines = [ln for ln in log.splitlines() if "packed-fp32-ops" not in ln]
             if lines:
                 print("\n".join(lines))
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--resource-usage", action="store_true")
+    ap.add_argument("-D", dest="defines", action="append", default=[], help="extra preprocessor definition")
+    ap.add_argument("--out", default=LIB, help="output library path")
+    ap.add_argument("--build-dir", default=BUILD)
     args = ap.parse_args(argv)
-    build(verbose=args.verbose, resource_usage=args.resource_usage)
+    build(verbose=args.verbose, resource_usage=args.resource_usage, defines=args.defines, out=args.out,
+          build_dir=args.build_dir)
 
 
 if __name__ == "__main__":

@@ -14,6 +14,10 @@ namespace {
 
 constexpr long long kMaxElems = (1LL << 31) - 1;
 constexpr int kMaxLen = 1 << 24;
+// One head's rows (L x D elements) must stay below 2^29 elements: the kernels
+// address a head through 32-bit byte offsets and mark out-of-range reads
+// with offsets at 2^31 and above.
+constexpr long long kMaxHeadElems = 1LL << 29;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -34,6 +38,7 @@ fa_status_t check_attn(int B, int Hq, int Hkv, int Lq, int Lkv, int D, float sca
     fa_status_t st = check_headdim(D, dt);
     if (st != FA_OK) return st;
     if ((long long)B * Hq * Lq * D > kMaxElems || (long long)B * Hkv * Lkv * D > kMaxElems) return FA_ERR_SHAPE;
+    if ((long long)Lq * D > kMaxHeadElems || (long long)Lkv * D > kMaxHeadElems) return FA_ERR_SHAPE;
     if (window < 0 || !std::isfinite(scale)) return FA_ERR_ARG;
     return FA_OK;
 }
@@ -74,12 +79,11 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
 
     fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Lq, Lkv, D,
                   (float)((double)scale * 1.4426950408889634), causal ? 1 : 0, effective_window(window, Lq)};
-    const int dmax = fa::dmax_bucket(D);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     switch (dtype) {
-        case FA_F32: return from_hip(fa::launch_fwd_f32(dmax, a, s));
-        case FA_F16: return from_hip(fa::launch_fwd_f16(dmax, a, s));
-        case FA_BF16: return from_hip(fa::launch_fwd_bf16(dmax, a, s));
+        case FA_F32: return from_hip(fa::launch_fwd_f32(a, s));
+        case FA_F16: return from_hip(fa::launch_fwd_f16(a, s));
+        case FA_BF16: return from_hip(fa::launch_fwd_bf16(a, s));
     }
     return FA_ERR_DTYPE;
 }
@@ -92,7 +96,7 @@ fa_status_t fa_bwd_preprocess(const void* o, const void* dO, float* delta, int B
     if (B < 1 || Hq < 1 || Lq < 1 || Lq >= kMaxLen) return FA_ERR_SHAPE;
     st = check_headdim(D, dtype);
     if (st != FA_OK) return st;
-    if ((long long)B * Hq * Lq * D > kMaxElems) return FA_ERR_SHAPE;
+    if ((long long)B * Hq * Lq * D > kMaxElems || (long long)Lq * D > kMaxHeadElems) return FA_ERR_SHAPE;
     if (!aligned16(o) || !aligned16(dO) || !aligned16(delta)) return FA_ERR_ALIGN;
 
     fa::PreArgs a{o, dO, delta, (long long)B * Hq * Lq, D};
@@ -129,12 +133,11 @@ fa_status_t fa_bwd_dkv(const void* q, const void* k, const void* v, const void* 
     fa::BwdArgs a{q, k, v, dO, lse, delta, nullptr, dk, dv, B, Hq, Hkv, Lq, Lkv, D,
                   (float)((double)scale * 1.4426950408889634), scale, causal ? 1 : 0,
                   effective_window(window, Lq)};
-    const int dmax = fa::dmax_bucket(D);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     switch (dtype) {
-        case FA_F32: return from_hip(fa::launch_dkv_f32(dmax, a, s));
-        case FA_F16: return from_hip(fa::launch_dkv_f16(dmax, a, s));
-        case FA_BF16: return from_hip(fa::launch_dkv_bf16(dmax, a, s));
+        case FA_F32: return from_hip(fa::launch_dkv_f32(a, s));
+        case FA_F16: return from_hip(fa::launch_dkv_f16(a, s));
+        case FA_BF16: return from_hip(fa::launch_dkv_bf16(a, s));
     }
     return FA_ERR_DTYPE;
 }
@@ -150,12 +153,11 @@ fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* d
     fa::BwdArgs a{q, k, v, dO, lse, delta, dq, nullptr, nullptr, B, Hq, Hkv, Lq, Lkv, D,
                   (float)((double)scale * 1.4426950408889634), scale, causal ? 1 : 0,
                   effective_window(window, Lq)};
-    const int dmax = fa::dmax_bucket(D);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     switch (dtype) {
-        case FA_F32: return from_hip(fa::launch_dq_f32(dmax, a, s));
-        case FA_F16: return from_hip(fa::launch_dq_f16(dmax, a, s));
-        case FA_BF16: return from_hip(fa::launch_dq_bf16(dmax, a, s));
+        case FA_F32: return from_hip(fa::launch_dq_f32(a, s));
+        case FA_F16: return from_hip(fa::launch_dq_f16(a, s));
+        case FA_BF16: return from_hip(fa::launch_dq_bf16(a, s));
     }
     return FA_ERR_DTYPE;
 }

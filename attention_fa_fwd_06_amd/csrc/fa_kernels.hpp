@@ -52,6 +52,7 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kLdsBudget = 160 * 1024;
+constexpr float kRescaleLog2 = 8.f;  // forward: move the reference max only past 2^8 growth
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
@@ -63,6 +64,16 @@ __device__ __forceinline__ f32x16 zero16() {
     for (int i = 0; i < 16; ++i) z[i] = 0.f;
     return z;
 }
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its outstanding global loads (which __syncthreads()
+// would drain), so loads for later tiles stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -273,7 +284,7 @@ __device__ __forceinline__ void reduce_partials(f32x16 (&x)[NB], float* red, int
         for (int q = 0; q < 4; ++q)
             r4[(((slot0 + dw) * NB + b) * 4 + q) * 64 + lane] =
                 f32x4{x[b][4 * q], x[b][4 * q + 1], x[b][4 * q + 2], x[b][4 * q + 3]};
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -317,8 +328,8 @@ template <class T, int DMAX, int BKV, int RW, int DW> struct FwdCfg {
     static_assert(DS % 32 == 0 && BKV % 32 == 0, "tile shape");
 };
 
-template <class T, int DMAX, int BKV, int RW, int DW>
-__global__ __launch_bounds__(64 * RW* DW) void fa_fwd_kernel(FwdArgs a) {
+template <class T, int DMAX, int BKV, int RW, int DW, int OCC>
+__global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_kernel(FwdArgs a) {
     using C = FwdCfg<T, DMAX, BKV, RW, DW>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -347,10 +358,20 @@ __global__ __launch_bounds__(64 * RW* DW) void fa_fwd_kernel(FwdArgs a) {
         qf[gi] = (row < a.Lq && c * C::E < a.D) ? ld16(qp + (size_t)row * a.D + c * C::E) : zero4();
     }
 
+    // A negative scale is folded into Q: negating bf16/f16/f32 values is exact,
+    // and it keeps the scaling factor c >= 0 for the row max below.
+    float c = a.c;
+    if (c < 0.f) {
+        c = -c;
+        const uint32_t sign = sizeof(T) == 2 ? 0x80008000u : 0x80000000u;
+#pragma unroll
+        for (int gi = 0; gi < C::NKG; ++gi) qf[gi] ^= sign;
+    }
+
     f32x16 o[C::NDB];
 #pragma unroll
     for (int i = 0; i < C::NDB; ++i) o[i] = zero16();
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_ref = -INFINITY, l_run = 0.f;
 
     // KV tiles that hold at least one allowed key for some row of this tile.
     const int i_last = min(i0 + C::BQ, a.Lq) - 1;
@@ -380,6 +401,7 @@ __global__ __launch_bounds__(64 * RW* DW) void fa_fwd_kernel(FwdArgs a) {
 
         const bool need = (t0 + BKV > a.Lkv) || (a.causal && t0 + BKV - 1 > i0) ||
                           (a.window && i_last - t0 >= a.window);
+        // Row max of the raw scores (c >= 0 here, so it commutes with the scaling).
         float mx = -INFINITY;
         if (need) {
 #pragma unroll
@@ -387,37 +409,56 @@ __global__ __launch_bounds__(64 * RW* DW) void fa_fwd_kernel(FwdArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int j = t0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const bool ok = j < a.Lkv && mask_ok(row, j, a.causal, a.window);
-                    s[kb][r] = ok ? s[kb][r] * a.c : -INFINITY;
+                    if (!(j < a.Lkv && mask_ok(row, j, a.causal, a.window))) s[kb][r] = -INFINITY;
                     mx = fmaxf(mx, s[kb][r]);
                 }
         } else {
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    s[kb][r] *= a.c;
-                    mx = fmaxf(mx, s[kb][r]);
-                }
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        // A tile with every score masked leaves the max at -inf; the offset 0
-        // keeps exp2(-inf - offset) = 0 instead of NaN.
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
+        const float m_tile = mx == -INFINITY ? -INFINITY : mx * c;
+        // The reference max moves only when a row's max grows by more than
+        // 2^kRescaleLog2: probabilities stay below 2^kRescaleLog2 and O is
+        // rescaled rarely. O, l and the LSE all use the same reference, so
+        // the result is the same up to rounding. A tile whose scores are all
+        // masked leaves the reference at -inf (no update, no NaN).
+        const bool upd = m_tile > m_ref + kRescaleLog2;
+        // Skipping the rescale for a whole wave pays off only where the branch
+        // does not force the accumulators through extra registers (OCC >= 2).
+        if (OCC < 2 || __ballot(upd)) {
+            const float m_new = upd ? m_tile : m_ref;
+            // 0 on a row's first update (O and l are still 0); 1 for rows that keep
+            // their reference, including rows still at -inf (no -inf - -inf).
+            const float alpha = upd ? fast_exp2(m_ref - m_new) : 1.f;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
+            m_ref = m_new;
+        }
+        const float moff = m_ref == -INFINITY ? 0.f : m_ref;
         float ls = 0.f;
+        if (need) {
 #pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
+            for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                s[kb][r] = fast_exp2(s[kb][r] - m_use);
-                ls += s[kb][r];
-            }
-        l_run = l_run * alpha + ls;
-        m_run = m_new;
+                for (int r = 0; r < 16; ++r) {
+                    const float sv = s[kb][r];
+                    s[kb][r] = sv == -INFINITY ? 0.f : fast_exp2(fmaf(sv, c, -moff));
+                    ls += s[kb][r];
+                }
+        } else {
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
+            for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    s[kb][r] = fast_exp2(fmaf(s[kb][r], c, -moff));
+                    ls += s[kb][r];
+                }
+        }
+        l_run += ls;
 
         PF<T> pf[C::NPG];
 #pragma unroll
@@ -478,7 +519,7 @@ __global__ __launch_bounds__(64 * RW* DW) void fa_fwd_kernel(FwdArgs a) {
                               o[db][4 * qd + 3] * inv);
             }
         if (h == 0 && dw == 0)
-            a.lse[(size_t)(b * a.Hq + hq) * a.Lq + row] = l > 0.f ? (m_run + fast_log2(l)) * kLn2 : -INFINITY;
+            a.lse[(size_t)(b * a.Hq + hq) * a.Lq + row] = l > 0.f ? (m_ref + fast_log2(l)) * kLn2 : -INFINITY;
     }
 }
 
@@ -542,8 +583,8 @@ template <class T, int DMAX, int BKV, int RW, int DW> struct DqCfg {
     static_assert(LDS <= kLdsBudget, "dQ tile does not fit in LDS");
 };
 
-template <class T, int DMAX, int BKV, int RW, int DW>
-__global__ __launch_bounds__(64 * RW* DW) void fa_dq_kernel(BwdArgs a) {
+template <class T, int DMAX, int BKV, int RW, int DW, int OCC>
+__global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_kernel(BwdArgs a) {
     using C = DqCfg<T, DMAX, BKV, RW, DW>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -719,8 +760,8 @@ template <class T, int DMAX, int BQ, int KW, int DW> struct DkvCfg {
     static_assert(LDS <= kLdsBudget, "dK/dV tile does not fit in LDS");
 };
 
-template <class T, int DMAX, int BQ, int KW, int DW>
-__global__ __launch_bounds__(64 * KW* DW) void fa_dkv_kernel(BwdArgs a) {
+template <class T, int DMAX, int BQ, int KW, int DW, int OCC>
+__global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_kernel(BwdArgs a) {
     using C = DkvCfg<T, DMAX, BQ, KW, DW>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -908,10 +949,10 @@ template <class K> inline hipError_t set_lds(K kernel, int bytes) {
     return hipSuccess;
 }
 
-template <class T, int DMAX, int BKV, int RW, int DW>
+template <class T, int DMAX, int BKV, int RW, int DW, int OCC>
 hipError_t launch_fwd_cfg(const FwdArgs& a, hipStream_t s) {
     using C = FwdCfg<T, DMAX, BKV, RW, DW>;
-    auto kern = fa_fwd_kernel<T, DMAX, BKV, RW, DW>;
+    auto kern = fa_fwd_kernel<T, DMAX, BKV, RW, DW, OCC>;
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
     const long long nqt = (a.Lq + C::BQ - 1) / C::BQ;
@@ -920,10 +961,10 @@ hipError_t launch_fwd_cfg(const FwdArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <class T, int DMAX, int BKV, int RW, int DW>
+template <class T, int DMAX, int BKV, int RW, int DW, int OCC>
 hipError_t launch_dq_cfg(const BwdArgs& a, hipStream_t s) {
     using C = DqCfg<T, DMAX, BKV, RW, DW>;
-    auto kern = fa_dq_kernel<T, DMAX, BKV, RW, DW>;
+    auto kern = fa_dq_kernel<T, DMAX, BKV, RW, DW, OCC>;
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
     const long long nqt = (a.Lq + C::BQ - 1) / C::BQ;
@@ -932,10 +973,10 @@ hipError_t launch_dq_cfg(const BwdArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <class T, int DMAX, int BQ, int KW, int DW>
+template <class T, int DMAX, int BQ, int KW, int DW, int OCC>
 hipError_t launch_dkv_cfg(const BwdArgs& a, hipStream_t s) {
     using C = DkvCfg<T, DMAX, BQ, KW, DW>;
-    auto kern = fa_dkv_kernel<T, DMAX, BQ, KW, DW>;
+    auto kern = fa_dkv_kernel<T, DMAX, BQ, KW, DW, OCC>;
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
     const long long nkt = (a.Lkv + C::BKV - 1) / C::BKV;
@@ -955,46 +996,95 @@ template <class T> hipError_t launch_pre_t(const PreArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Head-dim buckets of this path: a runtime D is served by the smallest bucket
+// >= D, with the columns past D zero-filled on load and never stored.
+inline int dmax_bucket(int D) {
+    if (D <= 32) return 32;
+    if (D <= 64) return 64;
+    if (D <= 96) return 96;
+    if (D <= 128) return 128;
+    if (D <= 256) return 256;
+    return 512;
+}
+
+// Two waves per SIMD fit the 16-bit kernels' registers; float operands take
+// twice the registers and stay at one.
+template <class T> constexpr int kOcc2 = sizeof(T) == 2 ? 2 : 1;
+// float forward tiles at head dim 96/128 take 32 keys to stay within registers.
+template <class T> constexpr int kFwdBkv = sizeof(T) == 2 ? 64 : 32;
+
+// Tile configuration of the hot head dims: <KV or Q tile, waves along rows or
+// keys, waves along d, minimum waves per SIMD>. Overridable at build time for
+// tuning sweeps of the 16-bit kernels (e.g. -DFA_FWD_128=64,4,1,2).
+#ifndef FA_FWD_128
+#define FA_FWD_128 64, 4, 1, 2
+#endif
+#ifndef FA_DQ_128
+#define FA_DQ_128 32, 4, 1, 2
+#endif
+#ifndef FA_DKV_128
+#define FA_DKV_128 64, 4, 1, 1
+#endif
+#ifndef FA_FWD_256
+#define FA_FWD_256 32, 4, 1, 1
+#endif
+#ifndef FA_DQ_256
+#define FA_DQ_256 32, 4, 1, 1
+#endif
+#ifndef FA_DKV_256
+#define FA_DKV_256 64, 2, 2, 1
+#endif
+
 // Head dims up to 128 run one wave per d range; 256 and 512 split d in
 // slices of 128 over DW waves. float inputs stop at head dim 256: their
 // staged Q, dO, Q^T and dO^T tiles at 512 exceed the 160 KB of LDS.
 template <class T> hipError_t launch_fwd_t(int dmax, const FwdArgs& a, hipStream_t s) {
     switch (dmax) {
-        case 32: return launch_fwd_cfg<T, 32, 64, 4, 1>(a, s);
-        case 64: return launch_fwd_cfg<T, 64, 64, 4, 1>(a, s);
-        case 96: return launch_fwd_cfg<T, 96, 64, 4, 1>(a, s);
-        case 128: return launch_fwd_cfg<T, 128, 64, 4, 1>(a, s);
-        case 256: return launch_fwd_cfg<T, 256, 32, 2, 2>(a, s);
+        case 32: return launch_fwd_cfg<T, 32, 64, 4, 1, kOcc2<T>>(a, s);
+        case 64: return launch_fwd_cfg<T, 64, 64, 4, 1, kOcc2<T>>(a, s);
+        case 96: return launch_fwd_cfg<T, 96, kFwdBkv<T>, 4, 1, kOcc2<T>>(a, s);
+        case 128:
+            if constexpr (sizeof(T) == 2) return launch_fwd_cfg<T, 128, FA_FWD_128>(a, s);
+            else return launch_fwd_cfg<T, 128, 32, 4, 1, 1>(a, s);
+        case 256:
+            if constexpr (sizeof(T) == 2) return launch_fwd_cfg<T, 256, FA_FWD_256>(a, s);
+            else return launch_fwd_cfg<T, 256, 32, 2, 2, 1>(a, s);
         case 512:
-            if constexpr (sizeof(T) == 2) return launch_fwd_cfg<T, 512, 32, 1, 4>(a, s);
+            if constexpr (sizeof(T) == 2) return launch_fwd_cfg<T, 512, 32, 1, 4, 1>(a, s);
             break;
     }
     return hipErrorInvalidValue;
 }
 template <class T> hipError_t launch_dq_t(int dmax, const BwdArgs& a, hipStream_t s) {
     switch (dmax) {
-        case 32: return launch_dq_cfg<T, 32, 64, 4, 1>(a, s);
-        case 64: return launch_dq_cfg<T, 64, 64, 4, 1>(a, s);
-        case 96: return launch_dq_cfg<T, 96, 64, 4, 1>(a, s);
-        case 128: return launch_dq_cfg<T, 128, 64, 4, 1>(a, s);
-        case 256: return launch_dq_cfg<T, 256, 32, 2, 2>(a, s);
+        case 32: return launch_dq_cfg<T, 32, 32, 4, 1, kOcc2<T>>(a, s);
+        case 64: return launch_dq_cfg<T, 64, 32, 4, 1, kOcc2<T>>(a, s);
+        case 96: return launch_dq_cfg<T, 96, 32, 4, 1, kOcc2<T>>(a, s);
+        case 128:
+            if constexpr (sizeof(T) == 2) return launch_dq_cfg<T, 128, FA_DQ_128>(a, s);
+            else return launch_dq_cfg<T, 128, 64, 4, 1, 1>(a, s);
+        case 256:
+            if constexpr (sizeof(T) == 2) return launch_dq_cfg<T, 256, FA_DQ_256>(a, s);
+            else return launch_dq_cfg<T, 256, 32, 2, 2, 1>(a, s);
         case 512:
-            if constexpr (sizeof(T) == 2) return launch_dq_cfg<T, 512, 32, 1, 4>(a, s);
+            if constexpr (sizeof(T) == 2) return launch_dq_cfg<T, 512, 32, 1, 4, 1>(a, s);
             break;
     }
     return hipErrorInvalidValue;
 }
 template <class T> hipError_t launch_dkv_t(int dmax, const BwdArgs& a, hipStream_t s) {
     switch (dmax) {
-        case 32: return launch_dkv_cfg<T, 32, 64, 4, 1>(a, s);
-        case 64: return launch_dkv_cfg<T, 64, 64, 4, 1>(a, s);
-        case 96: return launch_dkv_cfg<T, 96, 64, 4, 1>(a, s);
-        case 128: return launch_dkv_cfg<T, 128, 64, 4, 1>(a, s);
+        case 32: return launch_dkv_cfg<T, 32, 64, 4, 1, 1>(a, s);
+        case 64: return launch_dkv_cfg<T, 64, 64, 4, 1, 1>(a, s);
+        case 96: return launch_dkv_cfg<T, 96, 64, 4, 1, 1>(a, s);
+        case 128:
+            if constexpr (sizeof(T) == 2) return launch_dkv_cfg<T, 128, FA_DKV_128>(a, s);
+            else return launch_dkv_cfg<T, 128, 64, 4, 1, 1>(a, s);
         case 256:
-            if constexpr (sizeof(T) == 2) return launch_dkv_cfg<T, 256, 32, 2, 2>(a, s);
-            return launch_dkv_cfg<T, 256, 32, 1, 2>(a, s);
+            if constexpr (sizeof(T) == 2) return launch_dkv_cfg<T, 256, FA_DKV_256>(a, s);
+            else return launch_dkv_cfg<T, 256, 32, 1, 2, 1>(a, s);
         case 512:
-            if constexpr (sizeof(T) == 2) return launch_dkv_cfg<T, 512, 32, 1, 4>(a, s);
+            if constexpr (sizeof(T) == 2) return launch_dkv_cfg<T, 512, 32, 1, 4, 1>(a, s);
             break;
     }
     return hipErrorInvalidValue;

@@ -1,0 +1,754 @@
+// gfx950 kernels for 16-bit inputs built on LDS DMA and transposing LDS reads.
+//
+// Same method and MFMA chains as fa_kernels.hpp (forward: S^T = K Q^T ->
+// O^T += V^T P^T; dQ: S^T, dP^T -> dQ^T += K^T dS^T; dK/dV: S, dP ->
+// dV^T += dO^T P, dK^T += Q^T dS), with three CDNA4 features doing the data
+// movement:
+//   * buffer_load_dwordx4 ... lds: each streamed tile goes from HBM straight
+//     into LDS (no staging registers, no LDS stores), NS stages deep. Per-head
+//     buffer descriptors make rows past the sequence end read as zero; the
+//     head-dim tail of a row is pointed out of range on purpose and reads as
+//     zero too.
+//   * ds_read_b64_tr_b16: the transposed operands (V^T, K^T, Q^T, dO^T) are
+//     read from the same row-major tile: within each 16-lane group, lane j
+//     receives element j%4 of the 8-byte pieces addressed by lanes j/4,
+//     4+j/4, 8+j/4 and 12+j/4. Lane m of a group therefore addresses row
+//     k0 + m/4, columns d0 + 4(m%4) .. +3, and receives rows k0..k0+3 of
+//     column d0 + m: four consecutive k of its own column.
+//   * Tiles are stored row-major with the 16-byte chunk index of row r XORed
+//     with swz(r) = 2(r%4) + (r/4)%2. Eight consecutive rows at one chunk (a
+//     natural 16-byte fragment read) hit eight different bank groups, and the
+//     4 rows x 32 bytes of one transposing read cover all 32 banks once.
+#pragma once
+
+#include "fa_kernels.hpp"
+
+namespace fa {
+namespace lds {
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+constexpr int kBufWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 descriptor word 3)
+constexpr uint32_t kOob = 0x80000000u;  // an offset past every per-head extent: reads as zero
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
+}
+__device__ __forceinline__ u32x4 buf_ld16(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ void dma16(rsrc_t r, char* lds_dst, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_dst, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(rsrc_t r, char* lds_dst, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_dst, 4, voff, 0, 0, 0);
+}
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (lgkm and export counters left unconstrained).
+template <int N> __device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
+// Transposed A fragment: rows k0..k0+3 and k0+8..k0+11 (k0 = 16g + 4h) of
+// column d = d0 + lane%32, from a row-major swizzled tile. `p` already holds
+// the lane's row, column and swizzle; `rowb` is the tile's row pitch.
+__device__ __forceinline__ u32x4 rd_tr(const char* p, int rowb) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 8 * rowb));
+    const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+    return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+// Per-lane byte offsets inside a row-major swizzled tile of pitch ROWB.
+//   nat[j] : row ln, chunk (2j + h) ^ swz(ln)          (natural fragment, j = g % 4)
+//   tr[x]  : row 4h + m/4, chunk (4x + 2(q%2) + (m%4)/2) ^ swz, byte 8(m%2)
+//            (transposed fragment of a 32-column block with parity x)
+struct TileOffs {
+    int nat[4];
+    int tr[2];
+    __device__ __forceinline__ void init(int lane, int rowb) {
+        const int h = lane >> 5, ln = lane & 31, q = lane >> 4, m = lane & 15;
+        const int sn = swz(ln);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) nat[j] = ln * rowb + (((2 * j + h) ^ sn) << 4);
+        const int row = 4 * h + (m >> 2);
+        const int st = swz(row);
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+            tr[x] = row * rowb + (((4 * x + 2 * (q & 1) + ((m & 3) >> 1)) ^ st) << 4) + 8 * (m & 1);
+    }
+    // natural fragment: 32-row block base rb0 (multiple of 32), chunk 2g + h + cb
+    // (cb a multiple of 8)
+    __device__ __forceinline__ int natural(int rb0, int g, int cb, int rowb) const {
+        return rb0 * rowb + nat[g & 3] + (((g >> 2) << 3) + cb) * 16;
+    }
+    // transposed fragment: 16-row group gg, 32-column block db, column base cb
+    // (in chunks, a multiple of 8)
+    __device__ __forceinline__ int transposed(int gg, int db, int cb, int rowb) const {
+        return 16 * gg * rowb + tr[db & 1] + (((db >> 1) << 3) + cb) * 16;
+    }
+};
+
+// LDS-DMA plan for an R x DMAX (16-bit) tile issued by NW waves: wave w owns
+// instructions w, w + NW, ...; instruction i fills bytes [1024 i, 1024 i + 1024)
+// of the tile with the 64 chunks whose swizzled position falls there.
+template <int R, int DMAX, int NW> struct DmaPlan {
+    static constexpr int NDC = DMAX / 8;
+    static constexpr int NI = R * NDC / 64;
+    static_assert(R * NDC % 64 == 0 && NI % NW == 0, "tile must split evenly into 1 KiB DMA pieces per wave");
+    static constexpr int NIW = NI / NW;
+    uint32_t voff[NIW];
+    __device__ __forceinline__ void init(int lane, int w, int D) {
+#pragma unroll
+        for (int n = 0; n < NIW; ++n) {
+            const int slot = 64 * (w + n * NW) + lane;
+            const int r = slot / NDC, p = slot % NDC;
+            const int c = p ^ swz(r);  // logical chunk stored at physical chunk p
+            voff[n] = (c * 8 < D) ? (uint32_t)((r * D + c * 8) * 2) : kOob;
+        }
+    }
+    // rows row0.. of the head described by `rs` (row pitch D elements) -> tile
+    __device__ __forceinline__ void issue(rsrc_t rs, char* tile, int row0, int D, int w) const {
+        const uint32_t add = (uint32_t)row0 * (uint32_t)D * 2u;
+#pragma unroll
+        for (int n = 0; n < NIW; ++n) dma16(rs, tile + (w + n * NW) * 1024, voff[n] + add);
+    }
+};
+
+// ===========================================================================
+// Forward
+// ===========================================================================
+template <class T, int DMAX, int BKV, int RW, int DW, int NS> struct Fwd2Cfg {
+    static constexpr int NW = RW * DW, NT = 64 * NW, BQ = 32 * RW;
+    static constexpr int DS = DMAX / DW, SCH = DS / 8, NKG = SCH / 2, NDB = DS / 32;
+    static constexpr int NKB = BKV / 32, NPG = BKV / 16;
+    static constexpr int ROWB = DMAX * 2, TILEB = BKV * ROWB, STAGEB = 2 * TILEB;
+    static constexpr int RED = DW > 1 ? RW * DW * NKB * 16 * 64 * 4 : 0;
+    static constexpr int LDS = NS * STAGEB + RED;
+    static_assert(LDS <= kLdsBudget, "forward stages do not fit in LDS");
+    static_assert(NS >= 2 && DMAX % 64 == 0 && DS % 32 == 0, "configuration");
+};
+
+template <class T, int DMAX, int BKV, int RW, int DW, int OCC, int NS>
+__global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a) {
+    using C = Fwd2Cfg<T, DMAX, BKV, RW, DW, NS>;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int h = lane >> 5, ln = lane & 31;
+    const int rw = w / DW, dw = w % DW;
+
+    const int nqt = (a.Lq + C::BQ - 1) / C::BQ;
+    const int BH = a.B * a.Hq;
+    int qt = blockIdx.x / BH;
+    const int bh = blockIdx.x % BH;
+    if (a.causal) qt = nqt - 1 - qt;  // heaviest query tiles first
+    const int b = bh / a.Hq, hq = bh % a.Hq;
+    const int g = hq / (a.Hq / a.Hkv);
+    const int i0 = qt * C::BQ;
+    const int row = i0 + 32 * rw + ln;
+    const int D = a.D;
+
+    const size_t qhead = (size_t)(b * a.Hq + hq) * a.Lq * D;
+    const size_t kvhead = (size_t)(b * a.Hkv + g) * a.Lkv * D;
+    const uint32_t kvbytes = (uint32_t)a.Lkv * (uint32_t)D * 2u;
+    const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + qhead, (uint32_t)a.Lq * (uint32_t)D * 2u);
+    const rsrc_t rk = make_rsrc(reinterpret_cast<const T*>(a.k) + kvhead, kvbytes);
+    const rsrc_t rv = make_rsrc(reinterpret_cast<const T*>(a.v) + kvhead, kvbytes);
+
+    // Q fragments of this wave's 32 rows and d slice (B operand of S^T = K Q^T);
+    // rows past Lq and the head-dim tail read as zero.
+    u32x4 qf[C::NKG];
+#pragma unroll
+    for (int gi = 0; gi < C::NKG; ++gi) {
+        const int c = dw * C::SCH + 2 * gi + h;
+        qf[gi] = buf_ld16(rq, c * 8 < D ? (uint32_t)((row * D + c * 8) * 2) : kOob);
+    }
+    float c = a.c;
+    if (c < 0.f) {  // fold a negative scale into Q (exact), so that c >= 0 below
+        c = -c;
+#pragma unroll
+        for (int gi = 0; gi < C::NKG; ++gi) qf[gi] ^= 0x80008000u;
+    }
+
+    f32x16 o[C::NDB];
+#pragma unroll
+    for (int i = 0; i < C::NDB; ++i) o[i] = zero16();
+    float m_ref = -INFINITY, l_run = 0.f;
+
+    const int i_last = min(i0 + C::BQ, a.Lq) - 1;
+    const int j_lo = a.window ? max(0, i0 - a.window + 1) : 0;
+    const int j_hi = a.causal ? min(i_last, a.Lkv - 1) : a.Lkv - 1;
+    const int t_lo = j_lo / BKV;
+    const int n_t = j_hi >= j_lo ? j_hi / BKV - t_lo + 1 : 0;
+
+    TileOffs to;
+    to.init(lane, C::ROWB);
+    DmaPlan<BKV, DMAX, C::NW> dma;
+    dma.init(lane, w, D);
+    float* red = reinterpret_cast<float*>(smem + NS * C::STAGEB);
+    const int cb = dw * C::SCH;  // chunk base of this wave's d slice
+
+    auto issue = [&](int t) {
+        char* st = smem + (t % NS) * C::STAGEB;
+        dma.issue(rk, st, (t_lo + t) * BKV, D, w);
+        dma.issue(rv, st + C::TILEB, (t_lo + t) * BKV, D, w);
+    };
+    constexpr int LPT = 2 * DmaPlan<BKV, DMAX, C::NW>::NIW;  // DMA instructions per tile per wave
+
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < n_t) issue(s);
+
+    for (int t = 0; t < n_t; ++t) {
+        if (t + NS - 2 < n_t) wait_vm<(NS - 2) * LPT>();
+        else wait_vm<0>();
+        lds_barrier();  // tile t visible to all waves; every wave is done with tile t-1
+        if (t + NS - 1 < n_t) issue(t + NS - 1);
+
+        const char* kl = smem + (t % NS) * C::STAGEB;
+        const char* vl = kl + C::TILEB;
+        const int t0 = (t_lo + t) * BKV;
+        f32x16 s[C::NKB];
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+            s[kb] = zero16();
+#pragma unroll
+            for (int gi = 0; gi < C::NKG; ++gi)
+                Mma<T>::nat(s[kb], ld16(kl + to.natural(32 * kb, gi, cb, C::ROWB)), qf[gi]);
+        }
+        if constexpr (DW > 1) reduce_partials<DW, C::NKB>(s, red, rw * DW, dw, lane);
+
+        const bool need = (t0 + BKV > a.Lkv) || (a.causal && t0 + BKV - 1 > i0) ||
+                          (a.window && i_last - t0 >= a.window);
+        float mx = -INFINITY;
+        if (need) {
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int j = t0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+                    if (!(j < a.Lkv && mask_ok(row, j, a.causal, a.window))) s[kb][r] = -INFINITY;
+                    mx = fmaxf(mx, s[kb][r]);
+                }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_tile = mx == -INFINITY ? -INFINITY : mx * c;
+        const bool upd = m_tile > m_ref + kRescaleLog2;
+        if (OCC < 2 || __ballot(upd)) {
+            const float m_new = upd ? m_tile : m_ref;
+            const float alpha = upd ? fast_exp2(m_ref - m_new) : 1.f;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
+            m_ref = m_new;
+        }
+        const float moff = m_ref == -INFINITY ? 0.f : m_ref;
+        float ls = 0.f;
+        if (need) {
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float sv = s[kb][r];
+                    s[kb][r] = sv == -INFINITY ? 0.f : fast_exp2(fmaf(sv, c, -moff));
+                    ls += s[kb][r];
+                }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    s[kb][r] = fast_exp2(fmaf(s[kb][r], c, -moff));
+                    ls += s[kb][r];
+                }
+        }
+        l_run += ls;
+
+        PF<T> pf[C::NPG];
+#pragma unroll
+        for (int gg = 0; gg < C::NPG; ++gg) pf[gg] = make_pf<T>(s[gg >> 1], gg & 1);
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int gg = 0; gg < C::NPG; ++gg)
+                Mma<T>::nat(o[db], rd_tr(vl + to.transposed(gg, db, cb, C::ROWB), C::ROWB), pf[gg].v);
+    }
+
+    const float l = l_run + __shfl_xor(l_run, 32);
+    if (row < a.Lq) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        T* op = reinterpret_cast<T*>(a.o) + qhead + (size_t)row * D;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const int d = dw * C::DS + 32 * db + 8 * qd + 4 * h;
+                if (d < D)
+                    store4<T>(op + d, o[db][4 * qd] * inv, o[db][4 * qd + 1] * inv, o[db][4 * qd + 2] * inv,
+                              o[db][4 * qd + 3] * inv);
+            }
+        if (h == 0 && dw == 0)
+            a.lse[(size_t)(b * a.Hq + hq) * a.Lq + row] = l > 0.f ? (m_ref + fast_log2(l)) * kLn2 : -INFINITY;
+    }
+}
+
+// ===========================================================================
+// dQ
+// ===========================================================================
+template <class T, int DMAX, int BKV, int RW, int DW, int NS> struct Dq2Cfg {
+    static constexpr int NW = RW * DW, NT = 64 * NW, BQ = 32 * RW;
+    static constexpr int DS = DMAX / DW, SCH = DS / 8, NKG = SCH / 2, NDB = DS / 32;
+    static constexpr int NKB = BKV / 32, NPG = BKV / 16;
+    static constexpr int ROWB = DMAX * 2, TILEB = BKV * ROWB, STAGEB = 2 * TILEB;
+    static constexpr int RED = DW > 1 ? 2 * RW * DW * NKB * 16 * 64 * 4 : 0;
+    static constexpr int LDS = NS * STAGEB + RED;
+    static_assert(LDS <= kLdsBudget, "dQ stages do not fit in LDS");
+    static_assert(NS >= 2 && DMAX % 64 == 0 && DS % 32 == 0, "configuration");
+};
+
+template <class T, int DMAX, int BKV, int RW, int DW, int OCC, int NS>
+__global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a) {
+    using C = Dq2Cfg<T, DMAX, BKV, RW, DW, NS>;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int h = lane >> 5, ln = lane & 31;
+    const int rw = w / DW, dw = w % DW;
+
+    const int nqt = (a.Lq + C::BQ - 1) / C::BQ;
+    const int BH = a.B * a.Hq;
+    int qt = blockIdx.x / BH;
+    const int bh = blockIdx.x % BH;
+    if (a.causal) qt = nqt - 1 - qt;
+    const int b = bh / a.Hq, hq = bh % a.Hq;
+    const int g = hq / (a.Hq / a.Hkv);
+    const int i0 = qt * C::BQ;
+    const int row = i0 + 32 * rw + ln;
+    const int D = a.D;
+
+    const size_t qhead = (size_t)(b * a.Hq + hq) * a.Lq * D;
+    const size_t kvhead = (size_t)(b * a.Hkv + g) * a.Lkv * D;
+    const uint32_t qbytes = (uint32_t)a.Lq * (uint32_t)D * 2u;
+    const uint32_t kvbytes = (uint32_t)a.Lkv * (uint32_t)D * 2u;
+    const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + qhead, qbytes);
+    const rsrc_t rdo = make_rsrc(reinterpret_cast<const T*>(a.dO) + qhead, qbytes);
+    const rsrc_t rk = make_rsrc(reinterpret_cast<const T*>(a.k) + kvhead, kvbytes);
+    const rsrc_t rv = make_rsrc(reinterpret_cast<const T*>(a.v) + kvhead, kvbytes);
+
+    u32x4 qf[C::NKG], df[C::NKG];
+#pragma unroll
+    for (int gi = 0; gi < C::NKG; ++gi) {
+        const int c = dw * C::SCH + 2 * gi + h;
+        const uint32_t off = c * 8 < D ? (uint32_t)((row * D + c * 8) * 2) : kOob;
+        qf[gi] = buf_ld16(rq, off);
+        df[gi] = buf_ld16(rdo, off);
+    }
+    const size_t lrow = (size_t)(b * a.Hq + hq) * a.Lq + row;
+    const float lse2 = row < a.Lq ? a.lse[lrow] * kLog2e : 0.f;
+    const float dl = row < a.Lq ? a.delta[lrow] : 0.f;
+
+    f32x16 acc[C::NDB];
+#pragma unroll
+    for (int i = 0; i < C::NDB; ++i) acc[i] = zero16();
+
+    const int i_last = min(i0 + C::BQ, a.Lq) - 1;
+    const int j_lo = a.window ? max(0, i0 - a.window + 1) : 0;
+    const int j_hi = a.causal ? min(i_last, a.Lkv - 1) : a.Lkv - 1;
+    const int t_lo = j_lo / BKV;
+    const int n_t = j_hi >= j_lo ? j_hi / BKV - t_lo + 1 : 0;
+
+    TileOffs to;
+    to.init(lane, C::ROWB);
+    DmaPlan<BKV, DMAX, C::NW> dma;
+    dma.init(lane, w, D);
+    float* red = reinterpret_cast<float*>(smem + NS * C::STAGEB);
+    const int cb = dw * C::SCH;
+
+    auto issue = [&](int t) {
+        char* st = smem + (t % NS) * C::STAGEB;
+        dma.issue(rk, st, (t_lo + t) * BKV, D, w);
+        dma.issue(rv, st + C::TILEB, (t_lo + t) * BKV, D, w);
+    };
+    constexpr int LPT = 2 * DmaPlan<BKV, DMAX, C::NW>::NIW;
+
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < n_t) issue(s);
+
+    for (int t = 0; t < n_t; ++t) {
+        if (t + NS - 2 < n_t) wait_vm<(NS - 2) * LPT>();
+        else wait_vm<0>();
+        lds_barrier();
+        if (t + NS - 1 < n_t) issue(t + NS - 1);
+
+        const char* kl = smem + (t % NS) * C::STAGEB;
+        const char* vl = kl + C::TILEB;
+        const int t0 = (t_lo + t) * BKV;
+        f32x16 s[C::NKB], dp[C::NKB];
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+            s[kb] = zero16();
+            dp[kb] = zero16();
+#pragma unroll
+            for (int gi = 0; gi < C::NKG; ++gi) {
+                const int off = to.natural(32 * kb, gi, cb, C::ROWB);
+                Mma<T>::nat(s[kb], ld16(kl + off), qf[gi]);
+                Mma<T>::nat(dp[kb], ld16(vl + off), df[gi]);
+            }
+        }
+        if constexpr (DW > 1) {
+            reduce_partials<DW, C::NKB>(s, red, rw * DW, dw, lane);
+            reduce_partials<DW, C::NKB>(dp, red + RW * DW * C::NKB * 16 * 64, rw * DW, dw, lane);
+        }
+        const bool need = (t0 + BKV > a.Lkv) || (a.causal && t0 + BKV - 1 > i0) ||
+                          (a.window && i_last - t0 >= a.window);
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float p = fast_exp2(fmaf(s[kb][r], a.c, -lse2));
+                if (need) {
+                    const int j = t0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+                    if (!(j < a.Lkv && mask_ok(row, j, a.causal, a.window))) p = 0.f;
+                }
+                s[kb][r] = p * (dp[kb][r] - dl);  // dS^T
+            }
+        PF<T> pf[C::NPG];
+#pragma unroll
+        for (int gg = 0; gg < C::NPG; ++gg) pf[gg] = make_pf<T>(s[gg >> 1], gg & 1);
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int gg = 0; gg < C::NPG; ++gg)
+                Mma<T>::nat(acc[db], rd_tr(kl + to.transposed(gg, db, cb, C::ROWB), C::ROWB), pf[gg].v);
+    }
+
+    if (row < a.Lq) {
+        T* op = reinterpret_cast<T*>(a.dq) + qhead + (size_t)row * D;
+        const float sc = a.scale;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const int d = dw * C::DS + 32 * db + 8 * qd + 4 * h;
+                if (d < D)
+                    store4<T>(op + d, acc[db][4 * qd] * sc, acc[db][4 * qd + 1] * sc, acc[db][4 * qd + 2] * sc,
+                              acc[db][4 * qd + 3] * sc);
+            }
+    }
+}
+
+// ===========================================================================
+// dK/dV: the workgroup owns BKV = 32*KW keys of one kv head (one per lane) and
+// walks every query tile of every query head of the group that can see them.
+// ===========================================================================
+template <class T, int DMAX, int BQ, int KW, int DW, int NS> struct Dkv2Cfg {
+    static constexpr int NW = KW * DW, NT = 64 * NW, BKV = 32 * KW;
+    static constexpr int DS = DMAX / DW, SCH = DS / 8, NKG = SCH / 2, NDB = DS / 32;
+    static constexpr int NRB = BQ / 32, NPG = BQ / 16;
+    static constexpr int ROWB = DMAX * 2, TILEB = BQ * ROWB;
+    static constexpr int ROWSB = 2 * BQ * 4;                    // lse and delta of the tile's rows
+    static constexpr int STAGEB = 2 * TILEB + ((ROWSB + 1023) / 1024) * 1024;
+    static constexpr int RED1 = DW > 1 ? KW * DW * NRB * 16 * 64 * 4 : 0;
+    // When two partial-sum buffers do not fit next to the stages, S and dP are
+    // reduced one after the other through one buffer (one more barrier).
+    static constexpr bool SEQ = NS * STAGEB + 2 * RED1 > kLdsBudget;
+    static constexpr int RED = SEQ ? RED1 : 2 * RED1;
+    static constexpr int LDS = NS * STAGEB + RED;
+    static_assert(LDS <= kLdsBudget, "dK/dV stages do not fit in LDS");
+    static_assert(NS >= 2 && DMAX % 64 == 0 && DS % 32 == 0 && BQ >= 32 && BQ <= 64, "configuration");
+};
+
+template <class T, int DMAX, int BQ, int KW, int DW, int OCC, int NS>
+__global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_lds_kernel(BwdArgs a) {
+    using C = Dkv2Cfg<T, DMAX, BQ, KW, DW, NS>;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int h = lane >> 5, ln = lane & 31;
+    const int kw = w / DW, dw = w % DW;
+
+    const int BG = a.B * a.Hkv;
+    const int kt_idx = blockIdx.x / BG;  // small key blocks (most work under causal) first
+    const int bg = blockIdx.x % BG;
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
+    const int reps = a.Hq / a.Hkv;
+    const int j0 = kt_idx * C::BKV;
+    const int key = j0 + 32 * kw + ln;
+    const int D = a.D;
+
+    const size_t kvhead = (size_t)(b * a.Hkv + g) * a.Lkv * D;
+    const uint32_t kvbytes = (uint32_t)a.Lkv * (uint32_t)D * 2u;
+    const uint32_t qbytes = (uint32_t)a.Lq * (uint32_t)D * 2u;
+    const rsrc_t rk = make_rsrc(reinterpret_cast<const T*>(a.k) + kvhead, kvbytes);
+    const rsrc_t rv = make_rsrc(reinterpret_cast<const T*>(a.v) + kvhead, kvbytes);
+
+    // K and V fragments of this lane's key and this wave's d slice
+    // (B operands of S = Q K^T and dP = dO V^T).
+    u32x4 kf[C::NKG], vf[C::NKG];
+#pragma unroll
+    for (int gi = 0; gi < C::NKG; ++gi) {
+        const int c = dw * C::SCH + 2 * gi + h;
+        const uint32_t off = c * 8 < D ? (uint32_t)((key * D + c * 8) * 2) : kOob;
+        kf[gi] = buf_ld16(rk, off);
+        vf[gi] = buf_ld16(rv, off);
+    }
+
+    f32x16 dk[C::NDB], dv[C::NDB];
+#pragma unroll
+    for (int i = 0; i < C::NDB; ++i) {
+        dk[i] = zero16();
+        dv[i] = zero16();
+    }
+
+    const int j_last = min(j0 + C::BKV, a.Lkv) - 1;
+    const int i_lo = a.causal ? j0 : 0;
+    const int i_hi = a.window ? min(a.Lq - 1, j_last + a.window - 1) : a.Lq - 1;
+    const int qt_lo = i_lo / BQ;
+    const int nqt = i_hi >= i_lo ? i_hi / BQ - qt_lo + 1 : 0;
+    const int n_it = nqt * reps;
+
+    TileOffs to;
+    to.init(lane, C::ROWB);
+    DmaPlan<BQ, DMAX, C::NW> dma;
+    dma.init(lane, w, D);
+    float* red = reinterpret_cast<float*>(smem + NS * C::STAGEB);
+    const int cb = dw * C::SCH;
+    // lse and delta of a query tile, one float per lane (rows past Lq read as
+    // zero): wave 0 fetches lse, wave WD delta.
+    constexpr int WD = C::NW > 1 ? 1 : 0;
+
+    auto issue = [&](int it) {
+        const int hq = g * reps + it / nqt;
+        const int q0 = (qt_lo + it % nqt) * BQ;
+        const size_t qhead = (size_t)(b * a.Hq + hq) * a.Lq * D;
+        const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + qhead, qbytes);
+        const rsrc_t rdo = make_rsrc(reinterpret_cast<const T*>(a.dO) + qhead, qbytes);
+        char* st = smem + (it % NS) * C::STAGEB;
+        dma.issue(rq, st, q0, D, w);
+        dma.issue(rdo, st + C::TILEB, q0, D, w);
+        const size_t lhead = (size_t)(b * a.Hq + hq) * a.Lq;
+        if (w == 0) {
+            const rsrc_t rl = make_rsrc(a.lse + lhead, (uint32_t)a.Lq * 4u);
+            if (lane < BQ) dma4(rl, st + 2 * C::TILEB, (uint32_t)(q0 + lane) * 4u);
+        }
+        if (w == WD) {
+            const rsrc_t rd = make_rsrc(a.delta + lhead, (uint32_t)a.Lq * 4u);
+            if (lane < BQ) dma4(rd, st + 2 * C::TILEB + BQ * 4, (uint32_t)(q0 + lane) * 4u);
+        }
+    };
+    constexpr int LPT = 2 * DmaPlan<BQ, DMAX, C::NW>::NIW;
+    // DMA instructions per tile of this wave: the Q and dO pieces, plus lse
+    // (wave 0) and delta (wave WD).
+    const int extra = (w == 0) + (w == WD);
+
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < n_it) issue(s);
+
+    for (int it = 0; it < n_it; ++it) {
+        if (it + NS - 2 < n_it) {
+            if (extra == 2) wait_vm<(NS - 2) * (LPT + 2)>();
+            else if (extra == 1) wait_vm<(NS - 2) * (LPT + 1)>();
+            else wait_vm<(NS - 2) * LPT>();
+        } else {
+            wait_vm<0>();
+        }
+        lds_barrier();
+        if (it + NS - 1 < n_it) issue(it + NS - 1);
+
+        const char* ql = smem + (it % NS) * C::STAGEB;
+        const char* dol = ql + C::TILEB;
+        const float* lf = reinterpret_cast<const float*>(ql + 2 * C::TILEB);
+        const int q0 = (qt_lo + it % nqt) * BQ;
+
+        f32x16 s[C::NRB], dp[C::NRB];
+#pragma unroll
+        for (int rb = 0; rb < C::NRB; ++rb) {
+            s[rb] = zero16();
+            dp[rb] = zero16();
+#pragma unroll
+            for (int gi = 0; gi < C::NKG; ++gi) {
+                const int off = to.natural(32 * rb, gi, cb, C::ROWB);
+                Mma<T>::nat(s[rb], ld16(ql + off), kf[gi]);
+                Mma<T>::nat(dp[rb], ld16(dol + off), vf[gi]);
+            }
+        }
+        if constexpr (DW > 1) {
+            reduce_partials<DW, C::NRB>(s, red, kw * DW, dw, lane);
+            if constexpr (C::SEQ) {
+                lds_barrier();  // every wave has read the S partials
+                reduce_partials<DW, C::NRB>(dp, red, kw * DW, dw, lane);
+            } else {
+                reduce_partials<DW, C::NRB>(dp, red + KW * DW * C::NRB * 16 * 64, kw * DW, dw, lane);
+            }
+        }
+        const bool need = (q0 + BQ > a.Lq) || (a.causal && j0 + C::BKV - 1 > q0) ||
+                          (a.window && min(q0 + BQ, a.Lq) - 1 - j0 >= a.window);
+#pragma unroll
+        for (int rb = 0; rb < C::NRB; ++rb)
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const int rl = 32 * rb + 8 * qd + 4 * h;  // first of the 4 rows this lane holds
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(lf + rl);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(lf + BQ + rl);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * qd + i;
+                    float p = fast_exp2(fmaf(s[rb][r], a.c, -l4[i] * kLog2e));
+                    if (need) {
+                        const int irow = q0 + rl + i;
+                        if (!(irow < a.Lq && mask_ok(irow, key, a.causal, a.window))) p = 0.f;
+                    }
+                    s[rb][r] = p;
+                    dp[rb][r] = p * (dp[rb][r] - d4[i]);  // dS
+                }
+            }
+        PF<T> pf[C::NPG], sf[C::NPG];
+#pragma unroll
+        for (int gg = 0; gg < C::NPG; ++gg) {
+            pf[gg] = make_pf<T>(s[gg >> 1], gg & 1);
+            sf[gg] = make_pf<T>(dp[gg >> 1], gg & 1);
+        }
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int gg = 0; gg < C::NPG; ++gg) {
+                const int off = to.transposed(gg, db, cb, C::ROWB);
+                Mma<T>::nat(dv[db], rd_tr(dol + off, C::ROWB), pf[gg].v);
+                Mma<T>::nat(dk[db], rd_tr(ql + off, C::ROWB), sf[gg].v);
+            }
+    }
+
+    if (key < a.Lkv) {
+        T* kop = reinterpret_cast<T*>(a.dk) + kvhead + (size_t)key * D;
+        T* vop = reinterpret_cast<T*>(a.dv) + kvhead + (size_t)key * D;
+        const float sc = a.scale;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const int d = dw * C::DS + 32 * db + 8 * qd + 4 * h;
+                if (d < D) {
+                    store4<T>(kop + d, dk[db][4 * qd] * sc, dk[db][4 * qd + 1] * sc, dk[db][4 * qd + 2] * sc,
+                              dk[db][4 * qd + 3] * sc);
+                    store4<T>(vop + d, dv[db][4 * qd], dv[db][4 * qd + 1], dv[db][4 * qd + 2], dv[db][4 * qd + 3]);
+                }
+            }
+    }
+}
+
+// ===========================================================================
+// Launchers
+// ===========================================================================
+template <class T, int DMAX, int BKV, int RW, int DW, int OCC, int NS>
+hipError_t launch_fwd2(const FwdArgs& a, hipStream_t s) {
+    using C = Fwd2Cfg<T, DMAX, BKV, RW, DW, NS>;
+    auto kern = fa_fwd_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS>;
+    hipError_t e = set_lds(kern, C::LDS);
+    if (e != hipSuccess) return e;
+    const long long grid = (long long)((a.Lq + C::BQ - 1) / C::BQ) * a.B * a.Hq;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), C::LDS, s, a);
+    return hipGetLastError();
+}
+template <class T, int DMAX, int BKV, int RW, int DW, int OCC, int NS>
+hipError_t launch_dq2(const BwdArgs& a, hipStream_t s) {
+    using C = Dq2Cfg<T, DMAX, BKV, RW, DW, NS>;
+    auto kern = fa_dq_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS>;
+    hipError_t e = set_lds(kern, C::LDS);
+    if (e != hipSuccess) return e;
+    const long long grid = (long long)((a.Lq + C::BQ - 1) / C::BQ) * a.B * a.Hq;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), C::LDS, s, a);
+    return hipGetLastError();
+}
+template <class T, int DMAX, int BQ, int KW, int DW, int OCC, int NS>
+hipError_t launch_dkv2(const BwdArgs& a, hipStream_t s) {
+    using C = Dkv2Cfg<T, DMAX, BQ, KW, DW, NS>;
+    auto kern = fa_dkv_lds_kernel<T, DMAX, BQ, KW, DW, OCC, NS>;
+    hipError_t e = set_lds(kern, C::LDS);
+    if (e != hipSuccess) return e;
+    const long long grid = (long long)((a.Lkv + C::BKV - 1) / C::BKV) * a.B * a.Hkv;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), C::LDS, s, a);
+    return hipGetLastError();
+}
+
+// Head-dim buckets of the 16-bit path: a tile row must be a multiple of 128
+// bytes for the swizzle, so D is served by 64, 128, 256 or 512 (columns past
+// D read as zero and are never stored).
+inline int dmax16(int D) { return D <= 64 ? 64 : D <= 128 ? 128 : D <= 256 ? 256 : 512; }
+
+// <tile, waves along rows/keys, waves along d, min waves per SIMD, stages>.
+// Overridable at build time for tuning sweeps (e.g. -DFA2_FWD_128=64,4,1,2,2).
+#ifndef FA2_FWD_64
+#define FA2_FWD_64 64, 4, 1, 2, 2
+#endif
+#ifndef FA2_FWD_128
+#define FA2_FWD_128 64, 4, 1, 2, 2
+#endif
+#ifndef FA2_FWD_256
+#define FA2_FWD_256 32, 4, 1, 1, 2
+#endif
+#ifndef FA2_FWD_512
+#define FA2_FWD_512 32, 1, 4, 1, 2
+#endif
+#ifndef FA2_DQ_64
+#define FA2_DQ_64 32, 4, 1, 2, 3
+#endif
+#ifndef FA2_DQ_128
+#define FA2_DQ_128 32, 4, 1, 2, 3
+#endif
+#ifndef FA2_DQ_256
+#define FA2_DQ_256 32, 4, 1, 1, 2
+#endif
+#ifndef FA2_DQ_512
+#define FA2_DQ_512 32, 1, 4, 1, 2
+#endif
+#ifndef FA2_DKV_64
+#define FA2_DKV_64 64, 4, 1, 1, 2
+#endif
+#ifndef FA2_DKV_128
+#define FA2_DKV_128 64, 4, 1, 1, 2
+#endif
+#ifndef FA2_DKV_256
+#define FA2_DKV_256 32, 2, 2, 1, 2
+#endif
+#ifndef FA2_DKV_512
+#define FA2_DKV_512 32, 1, 4, 1, 2
+#endif
+
+template <class T> hipError_t launch_fwd16(const FwdArgs& a, hipStream_t s) {
+    switch (dmax16(a.D)) {
+        case 64: return launch_fwd2<T, 64, FA2_FWD_64>(a, s);
+        case 128: return launch_fwd2<T, 128, FA2_FWD_128>(a, s);
+        case 256: return launch_fwd2<T, 256, FA2_FWD_256>(a, s);
+        default: return launch_fwd2<T, 512, FA2_FWD_512>(a, s);
+    }
+}
+template <class T> hipError_t launch_dq16(const BwdArgs& a, hipStream_t s) {
+    switch (dmax16(a.D)) {
+        case 64: return launch_dq2<T, 64, FA2_DQ_64>(a, s);
+        case 128: return launch_dq2<T, 128, FA2_DQ_128>(a, s);
+        case 256: return launch_dq2<T, 256, FA2_DQ_256>(a, s);
+        default: return launch_dq2<T, 512, FA2_DQ_512>(a, s);
+    }
+}
+template <class T> hipError_t launch_dkv16(const BwdArgs& a, hipStream_t s) {
+    switch (dmax16(a.D)) {
+        case 64: return launch_dkv2<T, 64, FA2_DKV_64>(a, s);
+        case 128: return launch_dkv2<T, 128, FA2_DKV_128>(a, s);
+        case 256: return launch_dkv2<T, 256, FA2_DKV_256>(a, s);
+        default: return launch_dkv2<T, 512, FA2_DKV_512>(a, s);
+    }
+}
+
+}  // namespace lds
+}  // namespace fa

@@ -46,31 +46,17 @@ struct BwdArgs {
     int window;
 };
 
-// Element-type tags understood by the launchers.
-enum class Ty { F32 = 0, F16 = 1, BF16 = 2 };
-
-// Head-dim buckets: a runtime D is served by the smallest bucket >= D, with
-// the columns past D zero-filled on load and never stored.
-inline int dmax_bucket(int D) {
-    if (D <= 32) return 32;
-    if (D <= 64) return 64;
-    if (D <= 96) return 96;
-    if (D <= 128) return 128;
-    if (D <= 256) return 256;
-    return 512;
-}
-
-hipError_t launch_fwd_f32(int dmax, const FwdArgs& a, hipStream_t s);
-hipError_t launch_fwd_f16(int dmax, const FwdArgs& a, hipStream_t s);
-hipError_t launch_fwd_bf16(int dmax, const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_pre_f32(const PreArgs& a, hipStream_t s);
 hipError_t launch_pre_f16(const PreArgs& a, hipStream_t s);
 hipError_t launch_pre_bf16(const PreArgs& a, hipStream_t s);
-hipError_t launch_dkv_f32(int dmax, const BwdArgs& a, hipStream_t s);
-hipError_t launch_dkv_f16(int dmax, const BwdArgs& a, hipStream_t s);
-hipError_t launch_dkv_bf16(int dmax, const BwdArgs& a, hipStream_t s);
-hipError_t launch_dq_f32(int dmax, const BwdArgs& a, hipStream_t s);
-hipError_t launch_dq_f16(int dmax, const BwdArgs& a, hipStream_t s);
-hipError_t launch_dq_bf16(int dmax, const BwdArgs& a, hipStream_t s);
+hipError_t launch_dkv_f32(const BwdArgs& a, hipStream_t s);
+hipError_t launch_dkv_f16(const BwdArgs& a, hipStream_t s);
+hipError_t launch_dkv_bf16(const BwdArgs& a, hipStream_t s);
+hipError_t launch_dq_f32(const BwdArgs& a, hipStream_t s);
+hipError_t launch_dq_f16(const BwdArgs& a, hipStream_t s);
+hipError_t launch_dq_bf16(const BwdArgs& a, hipStream_t s);
 
 }  // namespace fa

@@ -196,6 +196,8 @@ def main(argv=None):
     ap.add_argument("--workload", type=int, default=2, help="index into synth.WORKLOADS (default: the 2048-token GQA)")
     ap.add_argument("--also", type=str, default="3", help="comma list of extra workload indices reported inline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain elementwise copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -205,6 +207,17 @@ def main(argv=None):
         sys.exit(2)
 
     from synth import WORKLOADS
+
+    if args.copy_calibration:
+        import torch
+
+        n = args.copy_calibration * (1 << 20) // 4
+        x = torch.ones(n, device="cuda", dtype=torch.float32)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.neg(x, out=y)  # reads and writes exactly MIB MiB each
+        torch.cuda.synchronize()
+        del x, y
 
     w = WORKLOADS[args.workload]
     main_res = run(w, args.steps, args.warmup, not args.no_cpu_baseline)

@@ -52,7 +52,8 @@
  *
  * Limits: 1 <= B, Hq, Hkv, Lq, Lkv; Hq % Hkv == 0; 32 <= D <= 512 and
  * D % 8 == 0 (D <= 256 for FA_F32); window >= 0; scale finite; every pointer 16-byte aligned;
- * B*Hq*Lq*D and B*Hkv*Lkv*D below 2^31; Lq, Lkv below 2^24.
+ * B*Hq*Lq*D and B*Hkv*Lkv*D below 2^31; Lq*D and Lkv*D at most 2^29;
+ * Lq, Lkv below 2^24.
  */
 #ifndef FA_H
 #define FA_H

@@ -103,6 +103,8 @@ def test_dq_null_pointers(lib, which):
         (dict(Hq=6, Hkv=4), SHAPE),
         (dict(Lq=1 << 24), SHAPE),
         (dict(B=1 << 12, Hq=64, Hkv=64, Lq=1 << 12, Lkv=16, D=128), SHAPE),
+        (dict(Lq=(1 << 21) + 8, Lkv=64, D=256), SHAPE),
+        (dict(Lq=64, Lkv=(1 << 20) + 8, D=512), SHAPE),
         (dict(D=24), HEADDIM),
         (dict(D=36), HEADDIM),
         (dict(D=520), HEADDIM),
