@@ -15,10 +15,10 @@
 //     4+j/4, 8+j/4 and 12+j/4. Lane m of a group therefore addresses row
 //     k0 + m/4, columns d0 + 4(m%4) .. +3, and receives rows k0..k0+3 of
 //     column d0 + m: four consecutive k of its own column.
-//   * Tiles are stored row-major with the 16-byte chunk index of row r XORed
-//     with swz(r) = 2(r%4) + (r/4)%2. Eight consecutive rows at one chunk (a
-//     natural 16-byte fragment read) hit eight different bank groups, and the
-//     4 rows x 32 bytes of one transposing read cover all 32 banks once.
+//   * Tiles are stored row-major with the low bits of the 16-byte chunk index
+//     of row r XORed with a row-dependent swizzle (swz below), chosen for the
+//     64-bank LDS: the 16 rows of a natural 16-byte fragment read and the
+//     4 rows x 64 bytes of a transposing read each cover all banks once.
 #pragma once
 
 #include "fa_kernels.hpp"
@@ -46,7 +46,19 @@ __device__ __forceinline__ void dma16(rsrc_t r, char* lds_dst, uint32_t voff) {
 __device__ __forceinline__ void dma4(rsrc_t r, char* lds_dst, uint32_t voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_dst, 4, voff, 0, 0, 0);
 }
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// Chunk swizzle of row r for a tile of pitch ROWB bytes (LDS of 64 banks x
+// 4 bytes: 256 bytes per cycle). ROWB >= 256: XOR the low 4 chunk bits with
+// 4(r%4) + (r/4)%4, so 16 consecutive rows at one chunk hit 16 bank groups and
+// the 4 rows x 64 bytes of a transposing read (32 lanes) cover all 64 banks.
+// ROWB = 128 (two rows per 256 bytes): the same with i = r/2 over 3 bits.
+template <int ROWB> __device__ __forceinline__ int swz(int r) {
+    if constexpr (ROWB >= 256) {
+        return ((r & 3) << 2) | ((r >> 2) & 3);
+    } else {
+        const int i = r >> 1;
+        return ((i & 1) << 2) | ((i >> 1) & 3);
+    }
+}
 
 // Wait until at most N vector-memory operations of this wave are in flight
 // (lgkm and export counters left unconstrained).
@@ -55,43 +67,56 @@ template <int N> __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
 }
 
-// Transposed A fragment: rows k0..k0+3 and k0+8..k0+11 (k0 = 16g + 4h) of
-// column d = d0 + lane%32, from a row-major swizzled tile. `p` already holds
-// the lane's row, column and swizzle; `rowb` is the tile's row pitch.
-__device__ __forceinline__ u32x4 rd_tr(const char* p, int rowb) {
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 8 * rowb));
+// Transposed A fragment from two reads: `lo` at rows k0..k0+3 and `hi` at
+// rows k0+8..k0+11 (k0 = 16g + 4h) of column d = d0 + lane%32.
+__device__ __forceinline__ u32x4 rd_tr(const char* lo_p, const char* hi_p) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lo_p));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(hi_p));
     const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
     return u32x4{a[0], a[1], b[0], b[1]};
 }
 
+// Scheduling fence: keeps a chain's LDS reads ahead of its MFMAs, so that all
+// of them are in flight together and each MFMA waits only for its own
+// fragment (left alone, the scheduler serialises read -> wait -> MFMA).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // Per-lane byte offsets inside a row-major swizzled tile of pitch ROWB.
-//   nat[j] : row ln, chunk (2j + h) ^ swz(ln)          (natural fragment, j = g % 4)
-//   tr[x]  : row 4h + m/4, chunk (4x + 2(q%2) + (m%4)/2) ^ swz, byte 8(m%2)
-//            (transposed fragment of a 32-column block with parity x)
-struct TileOffs {
-    int nat[4];
-    int tr[2];
-    __device__ __forceinline__ void init(int lane, int rowb) {
+//   nat[j]   : row ln, logical chunk 2j + h            (natural fragment, j = g % NN)
+//   tr[x][e] : row 4h + m/4 + 8e, logical chunk 4x + 2(q%2) + (m%4)/2, byte 8(m%2)
+//              (transposed fragment: 32-column block with db % NX = x, half e)
+// The swizzle repeats every 16 rows and touches only the low bits of the chunk
+// index, so whole 16-row groups and whole swizzle spans are plain offsets.
+template <int ROWB> struct TileOffs {
+    static constexpr int NC = ROWB / 16;            // chunks per row
+    static constexpr int SPAN = NC >= 16 ? 16 : 8;  // chunks covered by the swizzle
+    static constexpr int NN = SPAN / 2;
+    static constexpr int NX = SPAN / 4;
+    int nat[NN];
+    int tr[NX][2];
+    __device__ __forceinline__ void init(int lane) {
         const int h = lane >> 5, ln = lane & 31, q = lane >> 4, m = lane & 15;
-        const int sn = swz(ln);
+        const int sn = swz<ROWB>(ln);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) nat[j] = ln * rowb + (((2 * j + h) ^ sn) << 4);
-        const int row = 4 * h + (m >> 2);
-        const int st = swz(row);
+        for (int j = 0; j < NN; ++j) nat[j] = ln * ROWB + (((2 * j + h) ^ sn) << 4);
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
-            tr[x] = row * rowb + (((4 * x + 2 * (q & 1) + ((m & 3) >> 1)) ^ st) << 4) + 8 * (m & 1);
+        for (int e = 0; e < 2; ++e) {
+            const int row = 4 * h + (m >> 2) + 8 * e;
+            const int st = swz<ROWB>(row);
+#pragma unroll
+            for (int x = 0; x < NX; ++x)
+                tr[x][e] = row * ROWB + (((4 * x + 2 * (q & 1) + ((m & 3) >> 1)) ^ st) << 4) + 8 * (m & 1);
+        }
     }
     // natural fragment: 32-row block base rb0 (multiple of 32), chunk 2g + h + cb
-    // (cb a multiple of 8)
-    __device__ __forceinline__ int natural(int rb0, int g, int cb, int rowb) const {
-        return rb0 * rowb + nat[g & 3] + (((g >> 2) << 3) + cb) * 16;
+    // (cb a multiple of SPAN)
+    __device__ __forceinline__ int natural(int rb0, int g, int cb) const {
+        return rb0 * ROWB + nat[g % NN] + ((g / NN) * SPAN + cb) * 16;
     }
-    // transposed fragment: 16-row group gg, 32-column block db, column base cb
-    // (in chunks, a multiple of 8)
-    __device__ __forceinline__ int transposed(int gg, int db, int cb, int rowb) const {
-        return 16 * gg * rowb + tr[db & 1] + (((db >> 1) << 3) + cb) * 16;
+    // transposed fragment, half e: 16-row group gg, 32-column block db, column
+    // base cb (in chunks, a multiple of SPAN)
+    __device__ __forceinline__ int transposed(int gg, int db, int cb, int e) const {
+        return 16 * gg * ROWB + tr[db % NX][e] + ((db / NX) * SPAN + cb) * 16;
     }
 };
 
@@ -109,7 +134,7 @@ template <int R, int DMAX, int NW> struct DmaPlan {
         for (int n = 0; n < NIW; ++n) {
             const int slot = 64 * (w + n * NW) + lane;
             const int r = slot / NDC, p = slot % NDC;
-            const int c = p ^ swz(r);  // logical chunk stored at physical chunk p
+            const int c = p ^ swz<DMAX * 2>(r);  // logical chunk stored at physical chunk p
             voff[n] = (c * 8 < D) ? (uint32_t)((r * D + c * 8) * 2) : kOob;
         }
     }
@@ -187,8 +212,8 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
     const int t_lo = j_lo / BKV;
     const int n_t = j_hi >= j_lo ? j_hi / BKV - t_lo + 1 : 0;
 
-    TileOffs to;
-    to.init(lane, C::ROWB);
+    TileOffs<C::ROWB> to;
+    to.init(lane);
     DmaPlan<BKV, DMAX, C::NW> dma;
     dma.init(lane, w, D);
     float* red = reinterpret_cast<float*>(smem + NS * C::STAGEB);
@@ -217,10 +242,13 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
         f32x16 s[C::NKB];
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) {
+            u32x4 kfr[C::NKG];
+#pragma unroll
+            for (int gi = 0; gi < C::NKG; ++gi) kfr[gi] = ld16(kl + to.natural(32 * kb, gi, cb));
+            sched_fence();
             s[kb] = zero16();
 #pragma unroll
-            for (int gi = 0; gi < C::NKG; ++gi)
-                Mma<T>::nat(s[kb], ld16(kl + to.natural(32 * kb, gi, cb, C::ROWB)), qf[gi]);
+            for (int gi = 0; gi < C::NKG; ++gi) Mma<T>::nat(s[kb], kfr[gi], qf[gi]);
         }
         if constexpr (DW > 1) reduce_partials<DW, C::NKB>(s, red, rw * DW, dw, lane);
 
@@ -279,10 +307,15 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
 #pragma unroll
         for (int gg = 0; gg < C::NPG; ++gg) pf[gg] = make_pf<T>(s[gg >> 1], gg & 1);
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
+        for (int db = 0; db < C::NDB; ++db) {
+            u32x4 vfr[C::NPG];
 #pragma unroll
             for (int gg = 0; gg < C::NPG; ++gg)
-                Mma<T>::nat(o[db], rd_tr(vl + to.transposed(gg, db, cb, C::ROWB), C::ROWB), pf[gg].v);
+                vfr[gg] = rd_tr(vl + to.transposed(gg, db, cb, 0), vl + to.transposed(gg, db, cb, 1));
+            sched_fence();
+#pragma unroll
+            for (int gg = 0; gg < C::NPG; ++gg) Mma<T>::nat(o[db], vfr[gg], pf[gg].v);
+        }
     }
 
     const float l = l_run + __shfl_xor(l_run, 32);
@@ -367,8 +400,8 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
     const int t_lo = j_lo / BKV;
     const int n_t = j_hi >= j_lo ? j_hi / BKV - t_lo + 1 : 0;
 
-    TileOffs to;
-    to.init(lane, C::ROWB);
+    TileOffs<C::ROWB> to;
+    to.init(lane);
     DmaPlan<BKV, DMAX, C::NW> dma;
     dma.init(lane, w, D);
     float* red = reinterpret_cast<float*>(smem + NS * C::STAGEB);
@@ -399,11 +432,22 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
         for (int kb = 0; kb < C::NKB; ++kb) {
             s[kb] = zero16();
             dp[kb] = zero16();
+            constexpr int H = C::NKG > 4 ? C::NKG / 2 : C::NKG;  // fragments per batch
 #pragma unroll
-            for (int gi = 0; gi < C::NKG; ++gi) {
-                const int off = to.natural(32 * kb, gi, cb, C::ROWB);
-                Mma<T>::nat(s[kb], ld16(kl + off), qf[gi]);
-                Mma<T>::nat(dp[kb], ld16(vl + off), df[gi]);
+            for (int g0 = 0; g0 < C::NKG; g0 += H) {
+                u32x4 kfr[H], vfr[H];
+#pragma unroll
+                for (int i = 0; i < H; ++i) {
+                    const int off = to.natural(32 * kb, g0 + i, cb);
+                    kfr[i] = ld16(kl + off);
+                    vfr[i] = ld16(vl + off);
+                }
+                sched_fence();
+#pragma unroll
+                for (int i = 0; i < H; ++i) {
+                    Mma<T>::nat(s[kb], kfr[i], qf[g0 + i]);
+                    Mma<T>::nat(dp[kb], vfr[i], df[g0 + i]);
+                }
             }
         }
         if constexpr (DW > 1) {
@@ -427,10 +471,15 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
 #pragma unroll
         for (int gg = 0; gg < C::NPG; ++gg) pf[gg] = make_pf<T>(s[gg >> 1], gg & 1);
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
+        for (int db = 0; db < C::NDB; ++db) {
+            u32x4 kfr[C::NPG];
 #pragma unroll
             for (int gg = 0; gg < C::NPG; ++gg)
-                Mma<T>::nat(acc[db], rd_tr(kl + to.transposed(gg, db, cb, C::ROWB), C::ROWB), pf[gg].v);
+                kfr[gg] = rd_tr(kl + to.transposed(gg, db, cb, 0), kl + to.transposed(gg, db, cb, 1));
+            sched_fence();
+#pragma unroll
+            for (int gg = 0; gg < C::NPG; ++gg) Mma<T>::nat(acc[db], kfr[gg], pf[gg].v);
+        }
     }
 
     if (row < a.Lq) {
@@ -517,8 +566,8 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_lds_kernel(BwdArgs a
     const int nqt = i_hi >= i_lo ? i_hi / BQ - qt_lo + 1 : 0;
     const int n_it = nqt * reps;
 
-    TileOffs to;
-    to.init(lane, C::ROWB);
+    TileOffs<C::ROWB> to;
+    to.init(lane);
     DmaPlan<BQ, DMAX, C::NW> dma;
     dma.init(lane, w, D);
     float* red = reinterpret_cast<float*>(smem + NS * C::STAGEB);
@@ -576,11 +625,22 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_lds_kernel(BwdArgs a
         for (int rb = 0; rb < C::NRB; ++rb) {
             s[rb] = zero16();
             dp[rb] = zero16();
+            constexpr int H = C::NKG > 4 ? C::NKG / 2 : C::NKG;  // fragments per batch
 #pragma unroll
-            for (int gi = 0; gi < C::NKG; ++gi) {
-                const int off = to.natural(32 * rb, gi, cb, C::ROWB);
-                Mma<T>::nat(s[rb], ld16(ql + off), kf[gi]);
-                Mma<T>::nat(dp[rb], ld16(dol + off), vf[gi]);
+            for (int g0 = 0; g0 < C::NKG; g0 += H) {
+                u32x4 qfr[H], dfr[H];
+#pragma unroll
+                for (int i = 0; i < H; ++i) {
+                    const int off = to.natural(32 * rb, g0 + i, cb);
+                    qfr[i] = ld16(ql + off);
+                    dfr[i] = ld16(dol + off);
+                }
+                sched_fence();
+#pragma unroll
+                for (int i = 0; i < H; ++i) {
+                    Mma<T>::nat(s[rb], qfr[i], kf[g0 + i]);
+                    Mma<T>::nat(dp[rb], dfr[i], vf[g0 + i]);
+                }
             }
         }
         if constexpr (DW > 1) {
@@ -620,13 +680,21 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_lds_kernel(BwdArgs a
             sf[gg] = make_pf<T>(dp[gg >> 1], gg & 1);
         }
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
+        for (int db = 0; db < C::NDB; ++db) {
+            u32x4 dofr[C::NPG], qfr[C::NPG];
 #pragma unroll
             for (int gg = 0; gg < C::NPG; ++gg) {
-                const int off = to.transposed(gg, db, cb, C::ROWB);
-                Mma<T>::nat(dv[db], rd_tr(dol + off, C::ROWB), pf[gg].v);
-                Mma<T>::nat(dk[db], rd_tr(ql + off, C::ROWB), sf[gg].v);
+                const int o0 = to.transposed(gg, db, cb, 0), o1 = to.transposed(gg, db, cb, 1);
+                dofr[gg] = rd_tr(dol + o0, dol + o1);
+                qfr[gg] = rd_tr(ql + o0, ql + o1);
             }
+            sched_fence();
+#pragma unroll
+            for (int gg = 0; gg < C::NPG; ++gg) {
+                Mma<T>::nat(dv[db], dofr[gg], pf[gg].v);
+                Mma<T>::nat(dk[db], qfr[gg], sf[gg].v);
+            }
+        }
     }
 
     if (key < a.Lkv) {
@@ -643,6 +711,222 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_lds_kernel(BwdArgs a
                               dk[db][4 * qd + 3] * sc);
                     store4<T>(vop + d, dv[db][4 * qd], dv[db][4 * qd + 1], dv[db][4 * qd + 2], dv[db][4 * qd + 3]);
                 }
+            }
+    }
+}
+
+// ===========================================================================
+// dK/dV, split across wave pairs. For each 32-key block two waves share the
+// work of one step: the dV wave computes S = Q K^T, P = exp(S - LSE) (masked
+// entries 0) and dV^T += dO^T P; the dK wave computes dP = dO V^T, takes P
+// from its partner through LDS, forms dS = P (dP - Delta) and dK^T += Q^T dS.
+// Each wave holds one of K/V, one accumulator set and one score block, so the
+// workgroup runs 2*KW waves at two waves per SIMD and one wave's exp/VALU
+// phase overlaps the other's MFMAs. Keys are still owned exclusively by the
+// workgroup (no atomics).
+// ===========================================================================
+template <class T, int DMAX, int BQ, int KW, int NS> struct DkvSplitCfg {
+    static constexpr int NW = 2 * KW, NT = 64 * NW, BKV = 32 * KW;
+    static constexpr int NKG = DMAX / 16, NDB = DMAX / 32, SCH = DMAX / 8;
+    static constexpr int NRB = BQ / 32, NPG = BQ / 16;
+    static constexpr int ROWB = DMAX * 2, TILEB = BQ * ROWB;
+    static constexpr int ROWSB = 2 * BQ * 4;
+    static constexpr int STAGEB = 2 * TILEB + ((ROWSB + 1023) / 1024) * 1024;
+    static constexpr int PBUF = KW * NRB * 16 * 64 * 4;  // P of every dV wave, fp32, lane-major
+    static constexpr int LDS = NS * STAGEB + PBUF;
+    static_assert(LDS <= kLdsBudget, "split dK/dV stages do not fit in LDS");
+    static_assert(NS >= 2 && DMAX % 64 == 0 && BQ >= 32 && BQ <= 64, "configuration");
+};
+
+template <class T, int DMAX, int BQ, int KW, int OCC, int NS>
+__global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_split_kernel(BwdArgs a) {
+    using C = DkvSplitCfg<T, DMAX, BQ, KW, NS>;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int h = lane >> 5, ln = lane & 31;
+    const bool vw = w < KW;  // dV wave (else dK wave)
+    const int kw = w % KW;
+
+    const int BG = a.B * a.Hkv;
+    const int kt_idx = blockIdx.x / BG;  // small key blocks (most work under causal) first
+    const int bg = blockIdx.x % BG;
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
+    const int reps = a.Hq / a.Hkv;
+    const int j0 = kt_idx * C::BKV;
+    const int key = j0 + 32 * kw + ln;
+    const int D = a.D;
+
+    const size_t kvhead = (size_t)(b * a.Hkv + g) * a.Lkv * D;
+    const uint32_t kvbytes = (uint32_t)a.Lkv * (uint32_t)D * 2u;
+    const uint32_t qbytes = (uint32_t)a.Lq * (uint32_t)D * 2u;
+
+    // dV wave: K fragments (B of S = Q K^T); dK wave: V fragments (B of dP = dO V^T)
+    const rsrc_t rkv = make_rsrc(reinterpret_cast<const T*>(vw ? a.k : a.v) + kvhead, kvbytes);
+    u32x4 bf[C::NKG];
+#pragma unroll
+    for (int gi = 0; gi < C::NKG; ++gi) {
+        const int c = 2 * gi + h;
+        bf[gi] = buf_ld16(rkv, c * 8 < D ? (uint32_t)((key * D + c * 8) * 2) : kOob);
+    }
+
+    f32x16 acc[C::NDB];  // dV^T (dV wave) or dK^T (dK wave)
+#pragma unroll
+    for (int i = 0; i < C::NDB; ++i) acc[i] = zero16();
+
+    const int j_last = min(j0 + C::BKV, a.Lkv) - 1;
+    const int i_lo = a.causal ? j0 : 0;
+    const int i_hi = a.window ? min(a.Lq - 1, j_last + a.window - 1) : a.Lq - 1;
+    const int qt_lo = i_lo / BQ;
+    const int nqt = i_hi >= i_lo ? i_hi / BQ - qt_lo + 1 : 0;
+    const int n_it = nqt * reps;
+
+    TileOffs<C::ROWB> to;
+    to.init(lane);
+    DmaPlan<BQ, DMAX, C::NW> dma;
+    dma.init(lane, w, D);
+    f32x4* pbuf = reinterpret_cast<f32x4*>(smem + NS * C::STAGEB) + kw * C::NRB * 4 * 64 + lane;
+    constexpr int WD = KW;  // delta is fetched by the first dK wave, lse by wave 0
+
+    // per-iteration head and query-tile counters (no divisions in the loop)
+    int hq_issue = g * reps, qt_issue = qt_lo;  // next tile to load
+    int q0 = qt_lo * BQ, qt_cur = qt_lo;        // tile being computed
+    auto issue = [&](int it) {
+        const size_t qhead = (size_t)(b * a.Hq + hq_issue) * a.Lq * D;
+        const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + qhead, qbytes);
+        const rsrc_t rdo = make_rsrc(reinterpret_cast<const T*>(a.dO) + qhead, qbytes);
+        char* st = smem + (it % NS) * C::STAGEB;
+        const int qrow = qt_issue * BQ;
+        dma.issue(rq, st, qrow, D, w);
+        dma.issue(rdo, st + C::TILEB, qrow, D, w);
+        const size_t lhead = (size_t)(b * a.Hq + hq_issue) * a.Lq;
+        if (w == 0) {
+            const rsrc_t rl = make_rsrc(a.lse + lhead, (uint32_t)a.Lq * 4u);
+            if (lane < BQ) dma4(rl, st + 2 * C::TILEB, (uint32_t)(qrow + lane) * 4u);
+        }
+        if (w == WD) {
+            const rsrc_t rd = make_rsrc(a.delta + lhead, (uint32_t)a.Lq * 4u);
+            if (lane < BQ) dma4(rd, st + 2 * C::TILEB + BQ * 4, (uint32_t)(qrow + lane) * 4u);
+        }
+        if (++qt_issue == qt_lo + nqt) {
+            qt_issue = qt_lo;
+            ++hq_issue;
+        }
+    };
+    constexpr int LPT = 2 * DmaPlan<BQ, DMAX, C::NW>::NIW;
+    const bool extra = (w == 0) || (w == WD);
+
+#pragma unroll
+    for (int s0 = 0; s0 < NS - 1; ++s0)
+        if (s0 < n_it) issue(s0);
+
+    for (int it = 0; it < n_it; ++it) {
+        if (it + NS - 2 < n_it) {
+            if (extra) wait_vm<(NS - 2) * (LPT + 1)>();
+            else wait_vm<(NS - 2) * LPT>();
+        } else {
+            wait_vm<0>();
+        }
+        lds_barrier();  // tile `it` visible to all waves; every wave is done with tile it-1
+        if (it + NS - 1 < n_it) issue(it + NS - 1);
+
+        const char* ql = smem + (it % NS) * C::STAGEB;
+        const char* dol = ql + C::TILEB;
+        const float* lf = reinterpret_cast<const float*>(ql + 2 * C::TILEB);
+
+        // phase 1: S (dV wave) or dP (dK wave), rows of this tile x this lane's key
+        const char* ab = vw ? ql : dol;
+        f32x16 x[C::NRB];
+#pragma unroll
+        for (int rb = 0; rb < C::NRB; ++rb) {
+            x[rb] = zero16();
+            u32x4 fr[C::NKG];
+#pragma unroll
+            for (int gi = 0; gi < C::NKG; ++gi) fr[gi] = ld16(ab + to.natural(32 * rb, gi, 0));
+            sched_fence();
+#pragma unroll
+            for (int gi = 0; gi < C::NKG; ++gi) Mma<T>::nat(x[rb], fr[gi], bf[gi]);
+        }
+
+        if (vw) {
+            const bool need = (q0 + BQ > a.Lq) || (a.causal && j0 + C::BKV - 1 > q0) ||
+                              (a.window && min(q0 + BQ, a.Lq) - 1 - j0 >= a.window);
+#pragma unroll
+            for (int rb = 0; rb < C::NRB; ++rb)
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd) {
+                    const int rl = 32 * rb + 8 * qd + 4 * h;  // first of the 4 rows this lane holds
+                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(lf + rl);
+                    f32x4 p4;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float p = fast_exp2(fmaf(x[rb][4 * qd + i], a.c, -l4[i] * kLog2e));
+                        if (need) {
+                            const int irow = q0 + rl + i;
+                            const bool ok = (irow < a.Lq) & mask_ok(irow, key, a.causal, a.window);
+                            p = ok ? p : 0.f;
+                        }
+                        x[rb][4 * qd + i] = p;
+                        p4[i] = p;
+                    }
+                    pbuf[(rb * 4 + qd) * 64] = p4;
+                }
+        }
+        lds_barrier();  // P of this tile visible to the dK waves
+
+        if (vw) {
+            PF<T> pf[C::NPG];
+#pragma unroll
+            for (int gg = 0; gg < C::NPG; ++gg) pf[gg] = make_pf<T>(x[gg >> 1], gg & 1);
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db) {
+                u32x4 fr[C::NPG];
+#pragma unroll
+                for (int gg = 0; gg < C::NPG; ++gg)
+                    fr[gg] = rd_tr(dol + to.transposed(gg, db, 0, 0), dol + to.transposed(gg, db, 0, 1));
+                sched_fence();
+#pragma unroll
+                for (int gg = 0; gg < C::NPG; ++gg) Mma<T>::nat(acc[db], fr[gg], pf[gg].v);
+            }
+        } else {
+#pragma unroll
+            for (int rb = 0; rb < C::NRB; ++rb)
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd) {
+                    const int rl = 32 * rb + 8 * qd + 4 * h;
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(lf + BQ + rl);
+                    const f32x4 p4 = pbuf[(rb * 4 + qd) * 64];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[rb][4 * qd + i] = p4[i] * (x[rb][4 * qd + i] - d4[i]);  // dS
+                }
+            PF<T> sf[C::NPG];
+#pragma unroll
+            for (int gg = 0; gg < C::NPG; ++gg) sf[gg] = make_pf<T>(x[gg >> 1], gg & 1);
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db) {
+                u32x4 fr[C::NPG];
+#pragma unroll
+                for (int gg = 0; gg < C::NPG; ++gg)
+                    fr[gg] = rd_tr(ql + to.transposed(gg, db, 0, 0), ql + to.transposed(gg, db, 0, 1));
+                sched_fence();
+#pragma unroll
+                for (int gg = 0; gg < C::NPG; ++gg) Mma<T>::nat(acc[db], fr[gg], sf[gg].v);
+            }
+        }
+        if (++qt_cur == qt_lo + nqt) qt_cur = qt_lo;
+        q0 = qt_cur * BQ;
+    }
+
+    if (key < a.Lkv) {
+        T* op = reinterpret_cast<T*>(vw ? a.dv : a.dk) + kvhead + (size_t)key * D;
+        const float sc = vw ? 1.f : a.scale;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const int d = 32 * db + 8 * qd + 4 * h;
+                if (d < D)
+                    store4<T>(op + d, acc[db][4 * qd] * sc, acc[db][4 * qd + 1] * sc, acc[db][4 * qd + 2] * sc,
+                              acc[db][4 * qd + 3] * sc);
             }
     }
 }
@@ -681,6 +965,17 @@ hipError_t launch_dkv2(const BwdArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <class T, int DMAX, int BQ, int KW, int OCC, int NS>
+hipError_t launch_dkv_split(const BwdArgs& a, hipStream_t s) {
+    using C = DkvSplitCfg<T, DMAX, BQ, KW, NS>;
+    auto kern = fa_dkv_split_kernel<T, DMAX, BQ, KW, OCC, NS>;
+    hipError_t e = set_lds(kern, C::LDS);
+    if (e != hipSuccess) return e;
+    const long long grid = (long long)((a.Lkv + C::BKV - 1) / C::BKV) * a.B * a.Hkv;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), C::LDS, s, a);
+    return hipGetLastError();
+}
+
 // Head-dim buckets of the 16-bit path: a tile row must be a multiple of 128
 // bytes for the swizzle, so D is served by 64, 128, 256 or 512 (columns past
 // D read as zero and are never stored).
@@ -701,22 +996,16 @@ inline int dmax16(int D) { return D <= 64 ? 64 : D <= 128 ? 128 : D <= 256 ? 256
 #define FA2_FWD_512 32, 1, 4, 1, 2
 #endif
 #ifndef FA2_DQ_64
-#define FA2_DQ_64 32, 4, 1, 2, 3
+#define FA2_DQ_64 64, 4, 1, 2, 2
 #endif
 #ifndef FA2_DQ_128
-#define FA2_DQ_128 32, 4, 1, 2, 3
+#define FA2_DQ_128 64, 4, 1, 2, 2
 #endif
 #ifndef FA2_DQ_256
-#define FA2_DQ_256 32, 4, 1, 1, 2
+#define FA2_DQ_256 64, 4, 1, 1, 2
 #endif
 #ifndef FA2_DQ_512
 #define FA2_DQ_512 32, 1, 4, 1, 2
-#endif
-#ifndef FA2_DKV_64
-#define FA2_DKV_64 64, 4, 1, 1, 2
-#endif
-#ifndef FA2_DKV_128
-#define FA2_DKV_128 64, 4, 1, 1, 2
 #endif
 #ifndef FA2_DKV_256
 #define FA2_DKV_256 32, 2, 2, 1, 2
@@ -741,10 +1030,17 @@ template <class T> hipError_t launch_dq16(const BwdArgs& a, hipStream_t s) {
         default: return launch_dq2<T, 512, FA2_DQ_512>(a, s);
     }
 }
+// Split dK/dV (wave pairs): <query tile, key blocks of 32, min waves per SIMD, stages>.
+#ifndef FA2_DKVS_64
+#define FA2_DKVS_64 64, 4, 2, 2
+#endif
+#ifndef FA2_DKVS_128
+#define FA2_DKVS_128 64, 4, 2, 2
+#endif
 template <class T> hipError_t launch_dkv16(const BwdArgs& a, hipStream_t s) {
     switch (dmax16(a.D)) {
-        case 64: return launch_dkv2<T, 64, FA2_DKV_64>(a, s);
-        case 128: return launch_dkv2<T, 128, FA2_DKV_128>(a, s);
+        case 64: return launch_dkv_split<T, 64, FA2_DKVS_64>(a, s);
+        case 128: return launch_dkv_split<T, 128, FA2_DKVS_128>(a, s);
         case 256: return launch_dkv2<T, 256, FA2_DKV_256>(a, s);
         default: return launch_dkv2<T, 512, FA2_DKV_512>(a, s);
     }
