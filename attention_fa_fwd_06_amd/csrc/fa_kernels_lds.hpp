@@ -76,6 +76,14 @@ __device__ __forceinline__ u32x4 rd_tr(const char* lo_p, const char* hi_p) {
     return u32x4{a[0], a[1], b[0], b[1]};
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2). Renumber them so that XCD x receives one contiguous range of the
+// logical order; the logical order groups all workgroups that share one
+// (batch, kv head) together, so each L2 holds the K/V (or Q/dO) of few groups.
+__device__ __forceinline__ int xcd_remap(int i, int n) {
+    return (n & 7) ? i : (i & 7) * (n >> 3) + (i >> 3);
+}
+
 // Scheduling fence: keeps a chain's LDS reads ahead of its MFMAs, so that all
 // of them are in flight together and each MFMA waits only for its own
 // fragment (left alone, the scheduler serialises read -> wait -> MFMA).
@@ -168,13 +176,17 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
     const int h = lane >> 5, ln = lane & 31;
     const int rw = w / DW, dw = w % DW;
 
+    // logical order: (batch, kv head) group, then query tile heaviest first,
+    // then the query heads of the group (which share every K/V tile)
     const int nqt = (a.Lq + C::BQ - 1) / C::BQ;
-    const int BH = a.B * a.Hq;
-    int qt = blockIdx.x / BH;
-    const int bh = blockIdx.x % BH;
-    if (a.causal) qt = nqt - 1 - qt;  // heaviest query tiles first
-    const int b = bh / a.Hq, hq = bh % a.Hq;
-    const int g = hq / (a.Hq / a.Hkv);
+    const int reps = a.Hq / a.Hkv;
+    const int L = xcd_remap(blockIdx.x, nqt * a.B * a.Hq);
+    const int r = L % reps;
+    int qt = (L / reps) % nqt;
+    const int grp = L / (reps * nqt);
+    if (a.causal) qt = nqt - 1 - qt;
+    const int b = grp / a.Hkv, g = grp % a.Hkv;
+    const int hq = g * reps + r;
     const int i0 = qt * C::BQ;
     const int row = i0 + 32 * rw + ln;
     const int D = a.D;
@@ -358,13 +370,16 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
     const int h = lane >> 5, ln = lane & 31;
     const int rw = w / DW, dw = w % DW;
 
+    // same logical order as the forward
     const int nqt = (a.Lq + C::BQ - 1) / C::BQ;
-    const int BH = a.B * a.Hq;
-    int qt = blockIdx.x / BH;
-    const int bh = blockIdx.x % BH;
+    const int reps = a.Hq / a.Hkv;
+    const int L = xcd_remap(blockIdx.x, nqt * a.B * a.Hq);
+    const int r = L % reps;
+    int qt = (L / reps) % nqt;
+    const int grp = L / (reps * nqt);
     if (a.causal) qt = nqt - 1 - qt;
-    const int b = bh / a.Hq, hq = bh % a.Hq;
-    const int g = hq / (a.Hq / a.Hkv);
+    const int b = grp / a.Hkv, g = grp % a.Hkv;
+    const int hq = g * reps + r;
     const int i0 = qt * C::BQ;
     const int row = i0 + 32 * rw + ln;
     const int D = a.D;
@@ -526,8 +541,12 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_lds_kernel(BwdArgs a
     const int h = lane >> 5, ln = lane & 31;
     const int kw = w / DW, dw = w % DW;
 
+    // Key blocks in dispatch order, small blocks (the most work under causal)
+    // first across all (batch, kv head) groups: grouping them per XCD would
+    // pair heavy blocks on the same CU, and the Q/dO a group re-reads does
+    // not fit one L2 anyway.
     const int BG = a.B * a.Hkv;
-    const int kt_idx = blockIdx.x / BG;  // small key blocks (most work under causal) first
+    const int kt_idx = blockIdx.x / BG;
     const int bg = blockIdx.x % BG;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
     const int reps = a.Hq / a.Hkv;
@@ -747,8 +766,12 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_split_kernel(BwdArgs a) 
     const bool vw = w < KW;  // dV wave (else dK wave)
     const int kw = w % KW;
 
+    // Key blocks in dispatch order, small blocks (the most work under causal)
+    // first across all (batch, kv head) groups: grouping them per XCD would
+    // pair heavy blocks on the same CU, and the Q/dO a group re-reads does
+    // not fit one L2 anyway.
     const int BG = a.B * a.Hkv;
-    const int kt_idx = blockIdx.x / BG;  // small key blocks (most work under causal) first
+    const int kt_idx = blockIdx.x / BG;
     const int bg = blockIdx.x % BG;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
     const int reps = a.Hq / a.Hkv;
@@ -990,7 +1013,7 @@ inline int dmax16(int D) { return D <= 64 ? 64 : D <= 128 ? 128 : D <= 256 ? 256
 #define FA2_FWD_128 64, 4, 1, 2, 2
 #endif
 #ifndef FA2_FWD_256
-#define FA2_FWD_256 32, 4, 1, 1, 2
+#define FA2_FWD_256 64, 4, 1, 1, 2
 #endif
 #ifndef FA2_FWD_512
 #define FA2_FWD_512 32, 1, 4, 1, 2
