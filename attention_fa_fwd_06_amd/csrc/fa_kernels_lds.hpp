@@ -22,6 +22,8 @@
 #pragma once
 
 #include "fa_kernels.hpp"
+#include <climits>
+#include <type_traits>
 
 namespace fa {
 namespace lds {
@@ -88,6 +90,14 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
 // of them are in flight together and each MFMA waits only for its own
 // fragment (left alone, the scheduler serialises read -> wait -> MFMA).
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+template <class T> struct Vec8;
+template <> struct Vec8<__bf16> {
+    typedef bf16x8 type;
+};
+template <> struct Vec8<_Float16> {
+    typedef f16x8 type;
+};
 
 // Per-lane byte offsets inside a row-major swizzled tile of pitch ROWB.
 //   nat[j]   : row ln, logical chunk 2j + h            (natural fragment, j = g % NN)
@@ -735,222 +745,278 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_lds_kernel(BwdArgs a
 }
 
 // ===========================================================================
-// dK/dV, split across wave pairs. For each 32-key block two waves share the
-// work of one step: the dV wave computes S = Q K^T, P = exp(S - LSE) (masked
-// entries 0) and dV^T += dO^T P; the dK wave computes dP = dO V^T, takes P
-// from its partner through LDS, forms dS = P (dP - Delta) and dK^T += Q^T dS.
-// Each wave holds one of K/V, one accumulator set and one score block, so the
-// workgroup runs 2*KW waves at two waves per SIMD and one wave's exp/VALU
-// phase overlaps the other's MFMAs. Keys are still owned exclusively by the
-// workgroup (no atomics).
+// dK/dV on wave pairs with one barrier per query tile. For each 32-key block
+// two waves share the work: the dV wave computes S = Q K^T, P = exp(S - LSE)
+// (masked entries 0) and dV^T += dO^T P; the dK wave computes dP = dO V^T,
+// takes P from its partner through LDS, forms dS = P (dP - Delta) and
+// dK^T += Q^T dS. Each wave holds one of K/V, one accumulator set and one
+// score block, so a SIMD runs one wave of each kind. Keys are owned by the
+// workgroup alone (no atomics).
+//
+// Query tiles go through a three-slot LDS ring. Step t first forms the score
+// products of tile t (and, on the dV wave, P); one barrier then publishes P,
+// makes tile t+1 (already landed) visible and frees the slot of tile t-1 for
+// the DMA of tile t+2; after it both waves update their accumulators from
+// tile t. The dV wave issues at a higher priority, so its exp phase runs
+// while the dK wave's products keep the matrix core busy. The LDS fragments
+// of the next product are requested before the MFMAs of the current one.
+//
+// Under a causal mask without window a workgroup may take key blocks p and
+// nkt-1-p, which gives every workgroup the same amount of work. Workgroups of
+// one (batch, kv head) are placed on one XCD, and query tiles run from the
+// last one down with heads innermost, so the workgroups of a group stream the
+// same Q/dO tiles at about the same time through that XCD's L2.
 // ===========================================================================
-template <class T, int DMAX, int BQ, int KW, int NS> struct DkvSplitCfg {
+template <class T, int DMAX, int BQ, int KW> struct DkvPipeCfg {
+    static constexpr int NS = 3;  // tile t (computing), t+1 (landed), t+2 (in flight)
     static constexpr int NW = 2 * KW, NT = 64 * NW, BKV = 32 * KW;
-    static constexpr int NKG = DMAX / 16, NDB = DMAX / 32, SCH = DMAX / 8;
+    static constexpr int NKG = DMAX / 16, NDB = DMAX / 32;
     static constexpr int NRB = BQ / 32, NPG = BQ / 16;
     static constexpr int ROWB = DMAX * 2, TILEB = BQ * ROWB;
-    static constexpr int ROWSB = 2 * BQ * 4;
+    static constexpr int ROWSB = 2 * BQ * 4;  // lse and delta of the tile's rows
     static constexpr int STAGEB = 2 * TILEB + ((ROWSB + 1023) / 1024) * 1024;
-    static constexpr int PBUF = KW * NRB * 16 * 64 * 4;  // P of every dV wave, fp32, lane-major
-    static constexpr int LDS = NS * STAGEB + PBUF;
-    static_assert(LDS <= kLdsBudget, "split dK/dV stages do not fit in LDS");
-    static_assert(NS >= 2 && DMAX % 64 == 0 && BQ >= 32 && BQ <= 64, "configuration");
+    static constexpr int PBUF = KW * NPG * 64 * 16;  // P of every dV wave as MFMA operands, lane-major
+    static constexpr int LDS = NS * STAGEB + 2 * PBUF;
+    static_assert(LDS <= kLdsBudget, "dK/dV stages do not fit in LDS");
+    static_assert(DMAX % 64 == 0 && (BQ == 32 || BQ == 64), "configuration");
 };
 
-template <class T, int DMAX, int BQ, int KW, int OCC, int NS>
-__global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_split_kernel(BwdArgs a) {
-    using C = DkvSplitCfg<T, DMAX, BQ, KW, NS>;
+template <class T, int DMAX, int BQ, int KW, int OCC, int PRIO>
+__global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, int pair) {
+    using C = DkvPipeCfg<T, DMAX, BQ, KW>;
+    using T8 = typename Vec8<T>::type;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: buffer descriptors below depend on it
     const int h = lane >> 5, ln = lane & 31;
     const bool vw = w < KW;  // dV wave (else dK wave)
     const int kw = w % KW;
+    if (PRIO && vw) __builtin_amdgcn_s_setprio(1);
 
-    // Key blocks in dispatch order, small blocks (the most work under causal)
-    // first across all (batch, kv head) groups: grouping them per XCD would
-    // pair heavy blocks on the same CU, and the Q/dO a group re-reads does
-    // not fit one L2 anyway.
-    const int BG = a.B * a.Hkv;
-    const int kt_idx = blockIdx.x / BG;
-    const int bg = blockIdx.x % BG;
-    const int b = bg / a.Hkv, g = bg % a.Hkv;
+    const int nkt = (a.Lkv + C::BKV - 1) / C::BKV;
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    int bg, kt0, kt1 = -1;
+    if (pair) {
+        const int np = (nkt + 1) >> 1;
+        bg = L / np;
+        kt0 = L - bg * np;
+        if (nkt - 1 - kt0 != kt0) kt1 = nkt - 1 - kt0;
+    } else {
+        bg = L / nkt;
+        kt0 = L - bg * nkt;
+    }
+    const int b = bg / a.Hkv, g = bg - b * a.Hkv;
     const int reps = a.Hq / a.Hkv;
-    const int j0 = kt_idx * C::BKV;
-    const int key = j0 + 32 * kw + ln;
     const int D = a.D;
-
     const size_t kvhead = (size_t)(b * a.Hkv + g) * a.Lkv * D;
     const uint32_t kvbytes = (uint32_t)a.Lkv * (uint32_t)D * 2u;
     const uint32_t qbytes = (uint32_t)a.Lq * (uint32_t)D * 2u;
-
     // dV wave: K fragments (B of S = Q K^T); dK wave: V fragments (B of dP = dO V^T)
     const rsrc_t rkv = make_rsrc(reinterpret_cast<const T*>(vw ? a.k : a.v) + kvhead, kvbytes);
-    u32x4 bf[C::NKG];
-#pragma unroll
-    for (int gi = 0; gi < C::NKG; ++gi) {
-        const int c = 2 * gi + h;
-        bf[gi] = buf_ld16(rkv, c * 8 < D ? (uint32_t)((key * D + c * 8) * 2) : kOob);
-    }
-
-    f32x16 acc[C::NDB];  // dV^T (dV wave) or dK^T (dK wave)
-#pragma unroll
-    for (int i = 0; i < C::NDB; ++i) acc[i] = zero16();
-
-    const int j_last = min(j0 + C::BKV, a.Lkv) - 1;
-    const int i_lo = a.causal ? j0 : 0;
-    const int i_hi = a.window ? min(a.Lq - 1, j_last + a.window - 1) : a.Lq - 1;
-    const int qt_lo = i_lo / BQ;
-    const int nqt = i_hi >= i_lo ? i_hi / BQ - qt_lo + 1 : 0;
-    const int n_it = nqt * reps;
 
     TileOffs<C::ROWB> to;
     to.init(lane);
     DmaPlan<BQ, DMAX, C::NW> dma;
     dma.init(lane, w, D);
-    f32x4* pbuf = reinterpret_cast<f32x4*>(smem + NS * C::STAGEB) + kw * C::NRB * 4 * 64 + lane;
     constexpr int WD = KW;  // delta is fetched by the first dK wave, lse by wave 0
+    char* const pbase = smem + C::NS * C::STAGEB + (kw * C::NPG * 64 + lane) * 16;
+    // allowed entries: query - key in [dlo, dhi)
+    const int dlo = a.causal ? 0 : INT_MIN;
+    const int dhi = a.window ? a.window : INT_MAX;
+    const int aoff = vw ? 0 : C::TILEB;  // phase-A operand: Q (dV wave) or dO (dK wave)
+    const int toff = vw ? C::TILEB : 0;  // phase-B operand (transposed): dO or Q
 
-    // per-iteration head and query-tile counters (no divisions in the loop)
-    int hq_issue = g * reps, qt_issue = qt_lo;  // next tile to load
-    int q0 = qt_lo * BQ, qt_cur = qt_lo;        // tile being computed
-    auto issue = [&](int it) {
-        const size_t qhead = (size_t)(b * a.Hq + hq_issue) * a.Lq * D;
-        const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + qhead, qbytes);
-        const rsrc_t rdo = make_rsrc(reinterpret_cast<const T*>(a.dO) + qhead, qbytes);
-        char* st = smem + (it % NS) * C::STAGEB;
-        const int qrow = qt_issue * BQ;
-        dma.issue(rq, st, qrow, D, w);
-        dma.issue(rdo, st + C::TILEB, qrow, D, w);
-        const size_t lhead = (size_t)(b * a.Hq + hq_issue) * a.Lq;
-        if (w == 0) {
-            const rsrc_t rl = make_rsrc(a.lse + lhead, (uint32_t)a.Lq * 4u);
-            if (lane < BQ) dma4(rl, st + 2 * C::TILEB, (uint32_t)(qrow + lane) * 4u);
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+        const int kt = pass ? kt1 : kt0;
+        if (kt < 0) break;
+        const int j0 = kt * C::BKV;
+        const int key = j0 + 32 * kw + ln;
+
+        u32x4 bf[C::NKG];
+#pragma unroll
+        for (int gi = 0; gi < C::NKG; ++gi) {
+            const int c = 2 * gi + h;
+            bf[gi] = buf_ld16(rkv, c * 8 < D ? (uint32_t)((key * D + c * 8) * 2) : kOob);
         }
-        if (w == WD) {
-            const rsrc_t rd = make_rsrc(a.delta + lhead, (uint32_t)a.Lq * 4u);
-            if (lane < BQ) dma4(rd, st + 2 * C::TILEB + BQ * 4, (uint32_t)(qrow + lane) * 4u);
-        }
-        if (++qt_issue == qt_lo + nqt) {
-            qt_issue = qt_lo;
-            ++hq_issue;
-        }
-    };
-    constexpr int LPT = 2 * DmaPlan<BQ, DMAX, C::NW>::NIW;
-    const bool extra = (w == 0) || (w == WD);
+        f32x16 acc[C::NDB];  // dV^T (dV wave) or dK^T (dK wave)
+#pragma unroll
+        for (int i = 0; i < C::NDB; ++i) acc[i] = zero16();
 
-#pragma unroll
-    for (int s0 = 0; s0 < NS - 1; ++s0)
-        if (s0 < n_it) issue(s0);
+        const int j_last = min(j0 + C::BKV, a.Lkv) - 1;
+        const int i_lo = a.causal ? j0 : 0;
+        const int i_hi = a.window ? min(a.Lq - 1, j_last + a.window - 1) : a.Lq - 1;
+        const int qt_lo = i_lo / BQ, qt_hi = i_hi / BQ;
+        const int n_it = i_hi >= i_lo ? (qt_hi - qt_lo + 1) * reps : 0;
 
-    for (int it = 0; it < n_it; ++it) {
-        if (it + NS - 2 < n_it) {
-            if (extra) wait_vm<(NS - 2) * (LPT + 1)>();
-            else wait_vm<(NS - 2) * LPT>();
-        } else {
-            wait_vm<0>();
-        }
-        lds_barrier();  // tile `it` visible to all waves; every wave is done with tile it-1
-        if (it + NS - 1 < n_it) issue(it + NS - 1);
+        // tiles in the order (query tile from qt_hi down) x (head of the group)
+        int hq_issue = g * reps, qt_issue = qt_hi, slot_issue = 0;
+        auto issue = [&]() {
+            const size_t qhead = (size_t)(b * a.Hq + hq_issue) * a.Lq * D;
+            const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + qhead, qbytes);
+            const rsrc_t rdo = make_rsrc(reinterpret_cast<const T*>(a.dO) + qhead, qbytes);
+            char* st = smem + slot_issue * C::STAGEB;
+            const int qrow = qt_issue * BQ;
+            dma.issue(rq, st, qrow, D, w);
+            dma.issue(rdo, st + C::TILEB, qrow, D, w);
+            const size_t lhead = (size_t)(b * a.Hq + hq_issue) * a.Lq;
+            if (w == 0) {
+                const rsrc_t rl = make_rsrc(a.lse + lhead, (uint32_t)a.Lq * 4u);
+                if (lane < BQ) dma4(rl, st + 2 * C::TILEB, (uint32_t)(qrow + lane) * 4u);
+            }
+            if (w == WD) {
+                const rsrc_t rd = make_rsrc(a.delta + lhead, (uint32_t)a.Lq * 4u);
+                if (lane < BQ) dma4(rd, st + 2 * C::TILEB + BQ * 4, (uint32_t)(qrow + lane) * 4u);
+            }
+            if (++hq_issue == (g + 1) * reps) {
+                hq_issue = g * reps;
+                --qt_issue;
+            }
+            slot_issue = slot_issue == C::NS - 1 ? 0 : slot_issue + 1;
+        };
 
-        const char* ql = smem + (it % NS) * C::STAGEB;
-        const char* dol = ql + C::TILEB;
-        const float* lf = reinterpret_cast<const float*>(ql + 2 * C::TILEB);
+        lds_barrier();  // the previous pass is done with every slot and P buffer
+        if (n_it > 0) issue();
+        if (n_it > 1) issue();
+        wait_vm<0>();
+        lds_barrier();
 
-        // phase 1: S (dV wave) or dP (dK wave), rows of this tile x this lane's key
-        const char* ab = vw ? ql : dol;
-        f32x16 x[C::NRB];
+        // row block 0 of the phase-A operand of the tile being computed
+        u32x4 fr0[C::NKG];
 #pragma unroll
-        for (int rb = 0; rb < C::NRB; ++rb) {
-            x[rb] = zero16();
-            u32x4 fr[C::NKG];
-#pragma unroll
-            for (int gi = 0; gi < C::NKG; ++gi) fr[gi] = ld16(ab + to.natural(32 * rb, gi, 0));
-            sched_fence();
-#pragma unroll
-            for (int gi = 0; gi < C::NKG; ++gi) Mma<T>::nat(x[rb], fr[gi], bf[gi]);
-        }
+        for (int gi = 0; gi < C::NKG; ++gi) fr0[gi] = ld16(smem + aoff + to.natural(0, gi, 0));
 
-        if (vw) {
-            const bool need = (q0 + BQ > a.Lq) || (a.causal && j0 + C::BKV - 1 > q0) ||
-                              (a.window && min(q0 + BQ, a.Lq) - 1 - j0 >= a.window);
+        int slot = 0, qt_cur = qt_hi, hq_cnt = 0;
+        for (int it = 0; it < n_it; ++it) {
+            const char* st = smem + slot * C::STAGEB;
+            const float* lf = reinterpret_cast<const float*>(st + 2 * C::TILEB);
+            const char* tb = st + toff;
+            char* pb = pbase + (it & 1) * C::PBUF;
+            const int q0 = qt_cur * BQ;
+
+            // phase A: S (dV wave) or dP (dK wave) of this tile's rows x this lane's key
+            f32x16 x[C::NRB];
+            u32x4 nx[C::NPG];  // first 32-column block of the phase-B operand
+            f32x4 rv[C::NRB][4];  // lse (dV wave) or delta (dK wave) of the rows this lane holds
+            {
+                u32x4 fr1[C::NKG];
+                if constexpr (C::NRB == 2) {
 #pragma unroll
-            for (int rb = 0; rb < C::NRB; ++rb)
-#pragma unroll
-                for (int qd = 0; qd < 4; ++qd) {
-                    const int rl = 32 * rb + 8 * qd + 4 * h;  // first of the 4 rows this lane holds
-                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(lf + rl);
-                    f32x4 p4;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float p = fast_exp2(fmaf(x[rb][4 * qd + i], a.c, -l4[i] * kLog2e));
-                        if (need) {
-                            const int irow = q0 + rl + i;
-                            const bool ok = (irow < a.Lq) & mask_ok(irow, key, a.causal, a.window);
-                            p = ok ? p : 0.f;
-                        }
-                        x[rb][4 * qd + i] = p;
-                        p4[i] = p;
-                    }
-                    pbuf[(rb * 4 + qd) * 64] = p4;
+                    for (int gi = 0; gi < C::NKG; ++gi) fr1[gi] = ld16(st + aoff + to.natural(32, gi, 0));
                 }
-        }
-        lds_barrier();  // P of this tile visible to the dK waves
+                sched_fence();
+                x[0] = zero16();
+#pragma unroll
+                for (int gi = 0; gi < C::NKG; ++gi) Mma<T>::nat(x[0], fr0[gi], bf[gi]);
+                sched_fence();
+#pragma unroll
+                for (int gg = 0; gg < C::NPG; ++gg)
+                    nx[gg] = rd_tr(tb + to.transposed(gg, 0, 0, 0), tb + to.transposed(gg, 0, 0, 1));
+                sched_fence();
+                if constexpr (C::NRB == 2) {
+                    x[1] = zero16();
+#pragma unroll
+                    for (int gi = 0; gi < C::NKG; ++gi) Mma<T>::nat(x[1], fr1[gi], bf[gi]);
+                }
+                sched_fence();
+                const float* rowv = lf + (vw ? 0 : BQ) + 4 * h;
+#pragma unroll
+                for (int rb = 0; rb < C::NRB; ++rb)
+#pragma unroll
+                    for (int qd = 0; qd < 4; ++qd)
+                        rv[rb][qd] = *reinterpret_cast<const f32x4*>(rowv + 32 * rb + 8 * qd);
+            }
 
-        if (vw) {
             PF<T> pf[C::NPG];
+            if (vw) {
+                // P = exp2(c S - log2(e) lse), masked entries 0; x[rb][4 qd + i] is
+                // row 32 rb + 8 qd + 4 h + i of the tile
+                auto probs = [&](auto masked) {
 #pragma unroll
-            for (int gg = 0; gg < C::NPG; ++gg) pf[gg] = make_pf<T>(x[gg >> 1], gg & 1);
+                    for (int rb = 0; rb < C::NRB; ++rb)
 #pragma unroll
-            for (int db = 0; db < C::NDB; ++db) {
-                u32x4 fr[C::NPG];
+                        for (int r = 0; r < 16; ++r) {
+                            float p = fast_exp2(fmaf(x[rb][r], a.c, -rv[rb][r >> 2][r & 3] * kLog2e));
+                            if constexpr (decltype(masked)::value) {
+                                const int irow = q0 + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3), dd = irow - key;
+                                p = ((irow < a.Lq) & (dd >= dlo) & (dd < dhi)) ? p : 0.f;
+                            }
+                            x[rb][r] = p;
+                        }
+                };
+                const bool need = (q0 + BQ > a.Lq) || (a.causal && j0 + C::BKV - 1 > q0) ||
+                                  (a.window && min(q0 + BQ, a.Lq) - 1 - j0 >= a.window);
+                if (need) probs(std::true_type{});
+                else probs(std::false_type{});
 #pragma unroll
-                for (int gg = 0; gg < C::NPG; ++gg)
-                    fr[gg] = rd_tr(dol + to.transposed(gg, db, 0, 0), dol + to.transposed(gg, db, 0, 1));
-                sched_fence();
-#pragma unroll
-                for (int gg = 0; gg < C::NPG; ++gg) Mma<T>::nat(acc[db], fr[gg], pf[gg].v);
-            }
-        } else {
-#pragma unroll
-            for (int rb = 0; rb < C::NRB; ++rb)
-#pragma unroll
-                for (int qd = 0; qd < 4; ++qd) {
-                    const int rl = 32 * rb + 8 * qd + 4 * h;
-                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(lf + BQ + rl);
-                    const f32x4 p4 = pbuf[(rb * 4 + qd) * 64];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) x[rb][4 * qd + i] = p4[i] * (x[rb][4 * qd + i] - d4[i]);  // dS
+                for (int gg = 0; gg < C::NPG; ++gg) {
+                    pf[gg] = make_pf<T>(x[gg >> 1], gg & 1);
+                    st16(pb + gg * 1024, pf[gg].v);
                 }
-            PF<T> sf[C::NPG];
+            }
+            wait_vm<0>();   // this wave's share of tile it+1
+            lds_barrier();  // P visible; tile it+1 visible; every wave is done with tile it-1
+            if (it + 2 < n_it) issue();
+
+            if (!vw) {
+                // dS = P (dP - Delta)
 #pragma unroll
-            for (int gg = 0; gg < C::NPG; ++gg) sf[gg] = make_pf<T>(x[gg >> 1], gg & 1);
+                for (int gg = 0; gg < C::NPG; ++gg) {
+                    const T8 pv = __builtin_bit_cast(T8, ld16(pb + gg * 1024));
+                    const int rb = gg >> 1, hf = gg & 1;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int r = 8 * hf + i;
+                        x[rb][r] = (float)pv[i] * (x[rb][r] - rv[rb][r >> 2][r & 3]);
+                    }
+                    pf[gg] = make_pf<T>(x[rb], hf);
+                }
+            }
+
+            // phase B: acc += (dO or Q)^T of this tile x (P or dS); the next
+            // tile's phase-A fragments are requested during the last block
+            const int nslot = slot == C::NS - 1 ? 0 : slot + 1;
 #pragma unroll
             for (int db = 0; db < C::NDB; ++db) {
-                u32x4 fr[C::NPG];
+                u32x4 nn[C::NPG];
+                if (db + 1 < C::NDB) {
 #pragma unroll
-                for (int gg = 0; gg < C::NPG; ++gg)
-                    fr[gg] = rd_tr(ql + to.transposed(gg, db, 0, 0), ql + to.transposed(gg, db, 0, 1));
+                    for (int gg = 0; gg < C::NPG; ++gg)
+                        nn[gg] = rd_tr(tb + to.transposed(gg, db + 1, 0, 0), tb + to.transposed(gg, db + 1, 0, 1));
+                } else {
+                    const char* an = smem + nslot * C::STAGEB + aoff;
+#pragma unroll
+                    for (int gi = 0; gi < C::NKG; ++gi) fr0[gi] = ld16(an + to.natural(0, gi, 0));
+                }
                 sched_fence();
 #pragma unroll
-                for (int gg = 0; gg < C::NPG; ++gg) Mma<T>::nat(acc[db], fr[gg], sf[gg].v);
+                for (int gg = 0; gg < C::NPG; ++gg) Mma<T>::nat(acc[db], nx[gg], pf[gg].v);
+                sched_fence();
+                if (db + 1 < C::NDB) {
+#pragma unroll
+                    for (int gg = 0; gg < C::NPG; ++gg) nx[gg] = nn[gg];
+                }
+            }
+            slot = nslot;
+            if (++hq_cnt == reps) {
+                hq_cnt = 0;
+                --qt_cur;
             }
         }
-        if (++qt_cur == qt_lo + nqt) qt_cur = qt_lo;
-        q0 = qt_cur * BQ;
-    }
 
-    if (key < a.Lkv) {
-        T* op = reinterpret_cast<T*>(vw ? a.dv : a.dk) + kvhead + (size_t)key * D;
-        const float sc = vw ? 1.f : a.scale;
+        if (key < a.Lkv) {
+            T* op = reinterpret_cast<T*>(vw ? a.dv : a.dk) + kvhead + (size_t)key * D;
+            const float sc = vw ? 1.f : a.scale;
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
+            for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                const int d = 32 * db + 8 * qd + 4 * h;
-                if (d < D)
-                    store4<T>(op + d, acc[db][4 * qd] * sc, acc[db][4 * qd + 1] * sc, acc[db][4 * qd + 2] * sc,
-                              acc[db][4 * qd + 3] * sc);
-            }
+                for (int qd = 0; qd < 4; ++qd) {
+                    const int d = 32 * db + 8 * qd + 4 * h;
+                    if (d < D)
+                        store4<T>(op + d, acc[db][4 * qd] * sc, acc[db][4 * qd + 1] * sc,
+                                  acc[db][4 * qd + 2] * sc, acc[db][4 * qd + 3] * sc);
+                }
+        }
     }
 }
 
@@ -988,14 +1054,21 @@ hipError_t launch_dkv2(const BwdArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <class T, int DMAX, int BQ, int KW, int OCC, int NS>
-hipError_t launch_dkv_split(const BwdArgs& a, hipStream_t s) {
-    using C = DkvSplitCfg<T, DMAX, BQ, KW, NS>;
-    auto kern = fa_dkv_split_kernel<T, DMAX, BQ, KW, OCC, NS>;
+// Pairing key blocks p and nkt-1-p balances the work of a causal mask
+// without window; it is used only while it still leaves a workgroup for each
+// of the 256 CUs.
+constexpr int kPairMinGrid = 256;
+template <class T, int DMAX, int BQ, int KW, int OCC, int PRIO>
+hipError_t launch_dkv_pipe(const BwdArgs& a, hipStream_t s) {
+    using C = DkvPipeCfg<T, DMAX, BQ, KW>;
+    auto kern = fa_dkv_pipe_kernel<T, DMAX, BQ, KW, OCC, PRIO>;
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
-    const long long grid = (long long)((a.Lkv + C::BKV - 1) / C::BKV) * a.B * a.Hkv;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), C::LDS, s, a);
+    const long long nkt = (a.Lkv + C::BKV - 1) / C::BKV;
+    const long long bg = (long long)a.B * a.Hkv;
+    const int pair = a.causal && !a.window && nkt >= 2 && (nkt + 1) / 2 * bg >= kPairMinGrid;
+    const long long grid = pair ? (nkt + 1) / 2 * bg : nkt * bg;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), C::LDS, s, a, pair);
     return hipGetLastError();
 }
 
@@ -1053,17 +1126,17 @@ template <class T> hipError_t launch_dq16(const BwdArgs& a, hipStream_t s) {
         default: return launch_dq2<T, 512, FA2_DQ_512>(a, s);
     }
 }
-// Split dK/dV (wave pairs): <query tile, key blocks of 32, min waves per SIMD, stages>.
+// dK/dV on wave pairs: <query tile, key blocks of 32, min waves per SIMD, dV-wave priority>.
 #ifndef FA2_DKVS_64
-#define FA2_DKVS_64 64, 4, 2, 2
+#define FA2_DKVS_64 64, 4, 2, 1
 #endif
 #ifndef FA2_DKVS_128
-#define FA2_DKVS_128 64, 4, 2, 2
+#define FA2_DKVS_128 64, 4, 2, 1
 #endif
 template <class T> hipError_t launch_dkv16(const BwdArgs& a, hipStream_t s) {
     switch (dmax16(a.D)) {
-        case 64: return launch_dkv_split<T, 64, FA2_DKVS_64>(a, s);
-        case 128: return launch_dkv_split<T, 128, FA2_DKVS_128>(a, s);
+        case 64: return launch_dkv_pipe<T, 64, FA2_DKVS_64>(a, s);
+        case 128: return launch_dkv_pipe<T, 128, FA2_DKVS_128>(a, s);
         case 256: return launch_dkv2<T, 256, FA2_DKV_256>(a, s);
         default: return launch_dkv2<T, 512, FA2_DKV_512>(a, s);
     }
