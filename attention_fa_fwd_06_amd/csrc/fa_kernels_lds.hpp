@@ -826,198 +826,221 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
     const int aoff = vw ? 0 : C::TILEB;  // phase-A operand: Q (dV wave) or dO (dK wave)
     const int toff = vw ? C::TILEB : 0;  // phase-B operand (transposed): dO or Q
 
-#pragma unroll 1
-    for (int pass = 0; pass < 2; ++pass) {
-        const int kt = pass ? kt1 : kt0;
-        if (kt < 0) break;
-        const int j0 = kt * C::BKV;
-        const int key = j0 + 32 * kw + ln;
+    // The two wave kinds run separate copies of the loop (same barriers in the
+    // same order), so each is register-allocated and scheduled on its own.
+    auto run = [&](auto role) {
+        constexpr bool V = decltype(role)::value;
+    #pragma unroll 1
+        for (int pass = 0; pass < 2; ++pass) {
+            const int kt = pass ? kt1 : kt0;
+            if (kt < 0) break;
+            const int j0 = kt * C::BKV;
+            const int key = j0 + 32 * kw + ln;
 
-        u32x4 bf[C::NKG];
-#pragma unroll
-        for (int gi = 0; gi < C::NKG; ++gi) {
-            const int c = 2 * gi + h;
-            bf[gi] = buf_ld16(rkv, c * 8 < D ? (uint32_t)((key * D + c * 8) * 2) : kOob);
-        }
-        f32x16 acc[C::NDB];  // dV^T (dV wave) or dK^T (dK wave)
-#pragma unroll
-        for (int i = 0; i < C::NDB; ++i) acc[i] = zero16();
-
-        const int j_last = min(j0 + C::BKV, a.Lkv) - 1;
-        const int i_lo = a.causal ? j0 : 0;
-        const int i_hi = a.window ? min(a.Lq - 1, j_last + a.window - 1) : a.Lq - 1;
-        const int qt_lo = i_lo / BQ, qt_hi = i_hi / BQ;
-        const int n_it = i_hi >= i_lo ? (qt_hi - qt_lo + 1) * reps : 0;
-
-        // tiles in the order (query tile from qt_hi down) x (head of the group)
-        int hq_issue = g * reps, qt_issue = qt_hi, slot_issue = 0;
-        auto issue = [&]() {
-            const size_t qhead = (size_t)(b * a.Hq + hq_issue) * a.Lq * D;
-            const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + qhead, qbytes);
-            const rsrc_t rdo = make_rsrc(reinterpret_cast<const T*>(a.dO) + qhead, qbytes);
-            char* st = smem + slot_issue * C::STAGEB;
-            const int qrow = qt_issue * BQ;
-            dma.issue(rq, st, qrow, D, w);
-            dma.issue(rdo, st + C::TILEB, qrow, D, w);
-            const size_t lhead = (size_t)(b * a.Hq + hq_issue) * a.Lq;
-            if (w == 0) {
-                const rsrc_t rl = make_rsrc(a.lse + lhead, (uint32_t)a.Lq * 4u);
-                if (lane < BQ) dma4(rl, st + 2 * C::TILEB, (uint32_t)(qrow + lane) * 4u);
+            u32x4 bf[C::NKG];
+    #pragma unroll
+            for (int gi = 0; gi < C::NKG; ++gi) {
+                const int c = 2 * gi + h;
+                bf[gi] = buf_ld16(rkv, c * 8 < D ? (uint32_t)((key * D + c * 8) * 2) : kOob);
             }
-            if (w == WD) {
-                const rsrc_t rd = make_rsrc(a.delta + lhead, (uint32_t)a.Lq * 4u);
-                if (lane < BQ) dma4(rd, st + 2 * C::TILEB + BQ * 4, (uint32_t)(qrow + lane) * 4u);
-            }
-            if (++hq_issue == (g + 1) * reps) {
-                hq_issue = g * reps;
-                --qt_issue;
-            }
-            slot_issue = slot_issue == C::NS - 1 ? 0 : slot_issue + 1;
-        };
+            f32x16 acc[C::NDB];  // dV^T (dV wave) or dK^T (dK wave)
+    #pragma unroll
+            for (int i = 0; i < C::NDB; ++i) acc[i] = zero16();
 
-        lds_barrier();  // the previous pass is done with every slot and P buffer
-        if (n_it > 0) issue();
-        if (n_it > 1) issue();
-        wait_vm<0>();
-        lds_barrier();
+            const int j_last = min(j0 + C::BKV, a.Lkv) - 1;
+            const int i_lo = a.causal ? j0 : 0;
+            const int i_hi = a.window ? min(a.Lq - 1, j_last + a.window - 1) : a.Lq - 1;
+            const int qt_lo = i_lo / BQ, qt_hi = i_hi / BQ;
+            const int n_it = i_hi >= i_lo ? (qt_hi - qt_lo + 1) * reps : 0;
 
-        // row block 0 of the phase-A operand of the tile being computed
-        u32x4 fr0[C::NKG];
-#pragma unroll
-        for (int gi = 0; gi < C::NKG; ++gi) fr0[gi] = ld16(smem + aoff + to.natural(0, gi, 0));
-
-        int slot = 0, qt_cur = qt_hi, hq_cnt = 0;
-        for (int it = 0; it < n_it; ++it) {
-            const char* st = smem + slot * C::STAGEB;
-            const float* lf = reinterpret_cast<const float*>(st + 2 * C::TILEB);
-            const char* tb = st + toff;
-            char* pb = pbase + (it & 1) * C::PBUF;
-            const int q0 = qt_cur * BQ;
-
-            // phase A: S (dV wave) or dP (dK wave) of this tile's rows x this lane's key
-            f32x16 x[C::NRB];
-            u32x4 nx[C::NPG];  // first 32-column block of the phase-B operand
-            f32x4 rv[C::NRB][4];  // lse (dV wave) or delta (dK wave) of the rows this lane holds
-            {
-                u32x4 fr1[C::NKG];
-                if constexpr (C::NRB == 2) {
-#pragma unroll
-                    for (int gi = 0; gi < C::NKG; ++gi) fr1[gi] = ld16(st + aoff + to.natural(32, gi, 0));
+            // tiles in the order (query tile from qt_hi down) x (head of the group)
+            int hq_issue = g * reps, qt_issue = qt_hi, slot_issue = 0;
+            auto issue = [&]() {
+                const size_t qhead = (size_t)(b * a.Hq + hq_issue) * a.Lq * D;
+                const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + qhead, qbytes);
+                const rsrc_t rdo = make_rsrc(reinterpret_cast<const T*>(a.dO) + qhead, qbytes);
+                char* st = smem + slot_issue * C::STAGEB;
+                const int qrow = qt_issue * BQ;
+                dma.issue(rq, st, qrow, D, w);
+                dma.issue(rdo, st + C::TILEB, qrow, D, w);
+                const size_t lhead = (size_t)(b * a.Hq + hq_issue) * a.Lq;
+                if (w == 0) {
+                    const rsrc_t rl = make_rsrc(a.lse + lhead, (uint32_t)a.Lq * 4u);
+                    if (lane < BQ) dma4(rl, st + 2 * C::TILEB, (uint32_t)(qrow + lane) * 4u);
                 }
-                sched_fence();
-                x[0] = zero16();
-#pragma unroll
-                for (int gi = 0; gi < C::NKG; ++gi) Mma<T>::nat(x[0], fr0[gi], bf[gi]);
-                sched_fence();
-#pragma unroll
-                for (int gg = 0; gg < C::NPG; ++gg)
-                    nx[gg] = rd_tr(tb + to.transposed(gg, 0, 0, 0), tb + to.transposed(gg, 0, 0, 1));
-                sched_fence();
-                if constexpr (C::NRB == 2) {
-                    x[1] = zero16();
-#pragma unroll
-                    for (int gi = 0; gi < C::NKG; ++gi) Mma<T>::nat(x[1], fr1[gi], bf[gi]);
+                if (w == WD) {
+                    const rsrc_t rd = make_rsrc(a.delta + lhead, (uint32_t)a.Lq * 4u);
+                    if (lane < BQ) dma4(rd, st + 2 * C::TILEB + BQ * 4, (uint32_t)(qrow + lane) * 4u);
                 }
-                sched_fence();
-                const float* rowv = lf + (vw ? 0 : BQ) + 4 * h;
-#pragma unroll
-                for (int rb = 0; rb < C::NRB; ++rb)
-#pragma unroll
-                    for (int qd = 0; qd < 4; ++qd)
-                        rv[rb][qd] = *reinterpret_cast<const f32x4*>(rowv + 32 * rb + 8 * qd);
-            }
+                if (++hq_issue == (g + 1) * reps) {
+                    hq_issue = g * reps;
+                    --qt_issue;
+                }
+                slot_issue = slot_issue == C::NS - 1 ? 0 : slot_issue + 1;
+            };
 
-            PF<T> pf[C::NPG];
-            if (vw) {
-                // P = exp2(c S - log2(e) lse), masked entries 0; x[rb][4 qd + i] is
-                // row 32 rb + 8 qd + 4 h + i of the tile
-                auto probs = [&](auto masked) {
-#pragma unroll
+            lds_barrier();  // the previous pass is done with every slot and P buffer
+            if (n_it > 0) issue();
+            if (n_it > 1) issue();
+            wait_vm<0>();
+            lds_barrier();
+
+            // row block 0 of the phase-A operand of the tile being computed
+            u32x4 fr0[C::NKG];
+    #pragma unroll
+            for (int gi = 0; gi < C::NKG; ++gi) fr0[gi] = ld16(smem + aoff + to.natural(0, gi, 0));
+
+            int slot = 0, qt_cur = qt_hi, hq_cnt = 0;
+            for (int it = 0; it < n_it; ++it) {
+                const char* st = smem + slot * C::STAGEB;
+                const float* lf = reinterpret_cast<const float*>(st + 2 * C::TILEB);
+                const char* tb = st + toff;
+                char* pb = pbase + (it & 1) * C::PBUF;
+                const int q0 = qt_cur * BQ;
+
+                // phase A: S (dV wave) or dP (dK wave) of this tile's rows x this lane's key.
+                // Row block 0's fragments are already here; row block 1's arrive in two
+                // halves, each requested one chain ahead of its use.
+                f32x16 x[C::NRB];
+                u32x4 nx[C::NDB];     // row group 0 of the phase-B operand, all column blocks
+                f32x4 rv[C::NRB][4];  // lse (dV wave) or delta (dK wave) of the rows this lane holds
+                {
+                    constexpr int HG = C::NKG / 2;
+                    u32x4 fr1[C::NKG];
+                    if constexpr (C::NRB == 2) {
+    #pragma unroll
+                        for (int gi = 0; gi < HG; ++gi) fr1[gi] = ld16(st + aoff + to.natural(32, gi, 0));
+                    }
+                    sched_fence();
+                    x[0] = zero16();
+    #pragma unroll
+                    for (int gi = 0; gi < C::NKG; ++gi) Mma<T>::nat(x[0], fr0[gi], bf[gi]);
+                    sched_fence();
+                    if constexpr (C::NRB == 2) {
+    #pragma unroll
+                        for (int gi = HG; gi < C::NKG; ++gi) fr1[gi] = ld16(st + aoff + to.natural(32, gi, 0));
+                    }
+    #pragma unroll
+                    for (int db = 0; db < C::NDB; ++db)
+                        nx[db] = rd_tr(tb + to.transposed(0, db, 0, 0), tb + to.transposed(0, db, 0, 1));
+                    sched_fence();
+                    if constexpr (C::NRB == 2) {
+                        x[1] = zero16();
+    #pragma unroll
+                        for (int gi = 0; gi < C::NKG; ++gi) Mma<T>::nat(x[1], fr1[gi], bf[gi]);
+                    }
+                    sched_fence();
+                    const float* rowv = lf + (V ? 0 : BQ) + 4 * h;
+    #pragma unroll
                     for (int rb = 0; rb < C::NRB; ++rb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            float p = fast_exp2(fmaf(x[rb][r], a.c, -rv[rb][r >> 2][r & 3] * kLog2e));
-                            if constexpr (decltype(masked)::value) {
-                                const int irow = q0 + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3), dd = irow - key;
-                                p = ((irow < a.Lq) & (dd >= dlo) & (dd < dhi)) ? p : 0.f;
-                            }
-                            x[rb][r] = p;
-                        }
-                };
-                const bool need = (q0 + BQ > a.Lq) || (a.causal && j0 + C::BKV - 1 > q0) ||
-                                  (a.window && min(q0 + BQ, a.Lq) - 1 - j0 >= a.window);
-                if (need) probs(std::true_type{});
-                else probs(std::false_type{});
-#pragma unroll
-                for (int gg = 0; gg < C::NPG; ++gg) {
-                    pf[gg] = make_pf<T>(x[gg >> 1], gg & 1);
-                    st16(pb + gg * 1024, pf[gg].v);
+    #pragma unroll
+                        for (int qd = 0; qd < 4; ++qd)
+                            rv[rb][qd] = *reinterpret_cast<const f32x4*>(rowv + 32 * rb + 8 * qd);
                 }
-            }
-            wait_vm<0>();   // this wave's share of tile it+1
-            lds_barrier();  // P visible; tile it+1 visible; every wave is done with tile it-1
-            if (it + 2 < n_it) issue();
 
-            if (!vw) {
-                // dS = P (dP - Delta)
-#pragma unroll
-                for (int gg = 0; gg < C::NPG; ++gg) {
+                PF<T> pf[C::NPG];
+                if constexpr (V) {
+                    // P = exp2(c S - log2(e) lse), masked entries 0; x[rb][4 qd + i] is
+                    // row 32 rb + 8 qd + 4 h + i of the tile
+                    auto probs = [&](auto masked) {
+    #pragma unroll
+                        for (int rb = 0; rb < C::NRB; ++rb)
+    #pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                float p = fast_exp2(fmaf(x[rb][r], a.c, -rv[rb][r >> 2][r & 3] * kLog2e));
+                                if constexpr (decltype(masked)::value) {
+                                    const int irow = q0 + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3), dd = irow - key;
+                                    p = ((irow < a.Lq) & (dd >= dlo) & (dd < dhi)) ? p : 0.f;
+                                }
+                                x[rb][r] = p;
+                            }
+                    };
+                    const bool need = (q0 + BQ > a.Lq) || (a.causal && j0 + C::BKV - 1 > q0) ||
+                                      (a.window && min(q0 + BQ, a.Lq) - 1 - j0 >= a.window);
+                    if (need) probs(std::true_type{});
+                    else probs(std::false_type{});
+    #pragma unroll
+                    for (int gg = 0; gg < C::NPG; ++gg) {
+                        pf[gg] = make_pf<T>(x[gg >> 1], gg & 1);
+                        st16(pb + gg * 1024, pf[gg].v);
+                    }
+                } else {
+                    // dP - Delta while the dV wave is still on its exp phase
+    #pragma unroll
+                    for (int rb = 0; rb < C::NRB; ++rb)
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r) x[rb][r] -= rv[rb][r >> 2][r & 3];
+                }
+                wait_vm<0>();   // this wave's share of tile it+1
+                lds_barrier();  // P visible; tile it+1 visible; every wave is done with tile it-1
+                if (it + 2 < n_it) issue();
+
+                // phase B: acc[db] += (dO or Q)^T (column block db, row group gg) x
+                // (P or dS) of row group gg, row groups outermost so that the NDB
+                // accumulator chains alternate. The next row group's fragments (after
+                // the last group: the next tile's phase-A fragments) are requested
+                // ahead of each group's MFMAs; the dK wave forms dS = P (dP - Delta)
+                // one row group ahead.
+                const int nslot = slot == C::NS - 1 ? 0 : slot + 1;
+                auto ds_group = [&](int gg) {
                     const T8 pv = __builtin_bit_cast(T8, ld16(pb + gg * 1024));
                     const int rb = gg >> 1, hf = gg & 1;
-#pragma unroll
+    #pragma unroll
                     for (int i = 0; i < 8; ++i) {
                         const int r = 8 * hf + i;
-                        x[rb][r] = (float)pv[i] * (x[rb][r] - rv[rb][r >> 2][r & 3]);
+                        x[rb][r] *= (float)pv[i];
                     }
                     pf[gg] = make_pf<T>(x[rb], hf);
+                };
+                if constexpr (!V) ds_group(0);
+    #pragma unroll
+                for (int gg = 0; gg < C::NPG; ++gg) {
+                    u32x4 nn[C::NDB];
+                    if (gg + 1 < C::NPG) {
+    #pragma unroll
+                        for (int db = 0; db < C::NDB; ++db)
+                            nn[db] = rd_tr(tb + to.transposed(gg + 1, db, 0, 0), tb + to.transposed(gg + 1, db, 0, 1));
+                    } else {
+                        const char* an = smem + nslot * C::STAGEB + aoff;
+    #pragma unroll
+                        for (int gi = 0; gi < C::NKG; ++gi) fr0[gi] = ld16(an + to.natural(0, gi, 0));
+                    }
+                    sched_fence();
+    #pragma unroll
+                    for (int db = 0; db < C::NDB; ++db) Mma<T>::nat(acc[db], nx[db], pf[gg].v);
+                    if constexpr (!V) {
+                        if (gg + 1 < C::NPG) ds_group(gg + 1);
+                    }
+                    sched_fence();
+                    if (gg + 1 < C::NPG) {
+    #pragma unroll
+                        for (int db = 0; db < C::NDB; ++db) nx[db] = nn[db];
+                    }
+                }
+                slot = nslot;
+                if (++hq_cnt == reps) {
+                    hq_cnt = 0;
+                    --qt_cur;
                 }
             }
 
-            // phase B: acc += (dO or Q)^T of this tile x (P or dS); the next
-            // tile's phase-A fragments are requested during the last block
-            const int nslot = slot == C::NS - 1 ? 0 : slot + 1;
-#pragma unroll
-            for (int db = 0; db < C::NDB; ++db) {
-                u32x4 nn[C::NPG];
-                if (db + 1 < C::NDB) {
-#pragma unroll
-                    for (int gg = 0; gg < C::NPG; ++gg)
-                        nn[gg] = rd_tr(tb + to.transposed(gg, db + 1, 0, 0), tb + to.transposed(gg, db + 1, 0, 1));
-                } else {
-                    const char* an = smem + nslot * C::STAGEB + aoff;
-#pragma unroll
-                    for (int gi = 0; gi < C::NKG; ++gi) fr0[gi] = ld16(an + to.natural(0, gi, 0));
-                }
-                sched_fence();
-#pragma unroll
-                for (int gg = 0; gg < C::NPG; ++gg) Mma<T>::nat(acc[db], nx[gg], pf[gg].v);
-                sched_fence();
-                if (db + 1 < C::NDB) {
-#pragma unroll
-                    for (int gg = 0; gg < C::NPG; ++gg) nx[gg] = nn[gg];
-                }
-            }
-            slot = nslot;
-            if (++hq_cnt == reps) {
-                hq_cnt = 0;
-                --qt_cur;
+            if (key < a.Lkv) {
+                T* op = reinterpret_cast<T*>(V ? a.dv : a.dk) + kvhead + (size_t)key * D;
+                const float sc = V ? 1.f : a.scale;
+    #pragma unroll
+                for (int db = 0; db < C::NDB; ++db)
+    #pragma unroll
+                    for (int qd = 0; qd < 4; ++qd) {
+                        const int d = 32 * db + 8 * qd + 4 * h;
+                        if (d < D)
+                            store4<T>(op + d, acc[db][4 * qd] * sc, acc[db][4 * qd + 1] * sc,
+                                      acc[db][4 * qd + 2] * sc, acc[db][4 * qd + 3] * sc);
+                    }
             }
         }
-
-        if (key < a.Lkv) {
-            T* op = reinterpret_cast<T*>(vw ? a.dv : a.dk) + kvhead + (size_t)key * D;
-            const float sc = vw ? 1.f : a.scale;
-#pragma unroll
-            for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-                for (int qd = 0; qd < 4; ++qd) {
-                    const int d = 32 * db + 8 * qd + 4 * h;
-                    if (d < D)
-                        store4<T>(op + d, acc[db][4 * qd] * sc, acc[db][4 * qd + 1] * sc,
-                                  acc[db][4 * qd + 2] * sc, acc[db][4 * qd + 3] * sc);
-                }
-        }
-    }
+    };
+    if (vw) run(std::true_type{});
+    else run(std::false_type{});
 }
 
 // ===========================================================================
