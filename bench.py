@@ -28,6 +28,39 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 METRIC = "fwd+bwd attention TFLOP/s and % of bf16 MFMA peak (1 GPU)"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the kernel sources and build flags: HBM byte counts taken
+    with rocprofv3 are reported only while this digest still matches."""
+    import hashlib
+
+    csrc = os.path.join(ROOT, "attention_fa_fwd_06_amd", "csrc")
+    hsh = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hpp", ".hip", ".cpp", ".h")):
+            hsh.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as fh:
+                hsh.update(fh.read())
+    with open(os.path.join(ROOT, "attention_fa_fwd_06_amd", "build.py"), "rb") as fh:
+        hsh.update(fh.read())
+    return hsh.hexdigest()
+
+
+def measured_traffic(workload_name: str, kernel: str):
+    """Calibrated HBM bytes per launch (FETCH_SIZE + WRITE_SIZE) of `kernel` on
+    `workload_name` from the committed counter summary, or None when there is
+    none or the kernels have changed since it was taken."""
+    path = os.path.join(PROFILES, f"hbm_traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256") != kernel_source_digest():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else float(k["bytes_per_launch"])
 
 
 def allowed_pairs(Lq: int, Lkv: int, causal: bool, window: int) -> int:
@@ -178,8 +211,11 @@ def run(w, steps, warmup, with_cpu):
     dom = max(("fa_fwd", "fa_bwd_dkv", "fa_bwd_dq"), key=lambda n: per[n])
     unit_flops = {"fa_fwd": f["fwd"], "fa_bwd_dkv": f["dkv"], "fa_bwd_dq": f["dq"]}[dom]
     achieved = unit_flops / (per[dom] * 1e-3) / 1e12
+    dom_bytes = {"fa_fwd": by["fwd"], "fa_bwd_dkv": by["dkv"], "fa_bwd_dq": by["dq"]}[dom]
     res["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                       "frac": achieved / peak, "traffic": None, "avg_ms": per[dom]}
+                       "frac": achieved / peak, "traffic": measured_traffic(w.name, dom),
+                       "traffic_unit": "HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
+                       "algorithmic_bytes": dom_bytes, "avg_ms": per[dom]}
     res["kernel_tflops"] = {n: unit_flops_n / (per[n] * 1e-3) / 1e12 for n, unit_flops_n in
                             (("fa_fwd", f["fwd"]), ("fa_bwd_dkv", f["dkv"]), ("fa_bwd_dq", f["dq"]))}
     res["pre_gbs"] = by["pre"] / (per["fa_bwd_preprocess"] * 1e-3) / 1e9
@@ -194,7 +230,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2, help="index into synth.WORKLOADS (default: the 2048-token GQA)")
-    ap.add_argument("--also", type=str, default="3", help="comma list of extra workload indices reported inline")
+    ap.add_argument("--also", type=str, default="0,1,3", help="comma list of extra workload indices reported inline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain elementwise copy of MIB MiB (reference for HBM byte counters)")
@@ -226,8 +262,12 @@ def main(argv=None):
         if idx == args.workload:
             continue
         r = run(WORKLOADS[idx], args.steps, args.warmup, False)
+        wb = r["bytes"]
         extra[WORKLOADS[idx].name] = {
             "ms_per_step": round(r["ms_per_step"], 4), "tflops": round(r["tflops"], 2),
+            # algorithmic HBM bytes of the four kernels over the step time (the
+            # small cases are launch- and latency-bound, not MFMA-bound)
+            "hbm_gbs": round((wb["fwd"] + wb["pre"] + wb["dkv"] + wb["dq"]) / (r["ms_per_step"] * 1e-3) / 1e9, 1),
             "tflops_formula": round(r["tflops_formula"], 2), "pct_peak": round(r["pct_peak"], 2),
             "per_kernel_ms": {k: round(v, 4) for k, v in r["per_kernel_ms"].items()},
             "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r["roofline"].items()},

@@ -1,4 +1,7 @@
 """Host-side logic of bench.py (no GPU): exact allowed-pair counts."""
+import json
+import os
+
 import numpy as np
 import pytest
 
@@ -29,3 +32,19 @@ def test_gpus_other_than_one_exit(capsys):
         bench.main(["--gpus", "2"])
     assert e.value.code == 2
     assert "one GPU" in capsys.readouterr().out
+
+
+def test_traffic_is_reported_only_for_the_kernels_it_was_measured_on(monkeypatch):
+    import bench
+
+    rec_path = os.path.join(bench.PROFILES, "hbm_traffic_bf16_causal_gqa4_L2048_D128.json")
+    if not os.path.exists(rec_path):
+        pytest.skip("no committed counter summary")
+    with open(rec_path) as fh:
+        rec = json.load(fh)
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda: rec["source_sha256"])
+    t = bench.measured_traffic("bf16_causal_gqa4_L2048_D128", "fa_bwd_dkv")
+    assert t == float(rec["kernels"]["fa_bwd_dkv"]["bytes_per_launch"]) and t > 0
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda: "0" * 64)
+    assert bench.measured_traffic("bf16_causal_gqa4_L2048_D128", "fa_bwd_dkv") is None
+    assert bench.measured_traffic("no_such_workload", "fa_bwd_dkv") is None
