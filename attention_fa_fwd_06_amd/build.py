@@ -19,6 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
+PROBE = os.path.join(PKG, "mfma_ceiling")
 ARCH = "gfx950"
 
 SOURCES = ["fa_api.cpp", "fa_kernels_f32.hip", "fa_kernels_f16.hip", "fa_kernels_bf16.hip"]
@@ -75,6 +76,12 @@ def build(verbose: bool = False, resource_usage: bool = False, defines=(), out: 
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, out)
+    if out == LIB:
+        # measurement helper: the sustained MFMA rate and clock of this GPU
+        cmd = [_hipcc(), *COMMON, os.path.join(CSRC, "mfma_ceiling.hip"), "-o", PROBE]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     if verbose or resource_usage:
         for log in logs:
             lines = [ln for ln in log.splitlines() if "packed-fp32-ops" not in ln]

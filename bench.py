@@ -32,19 +32,19 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_digest() -> str:
-    """sha256 over the kernel sources and build flags: HBM byte counts taken
-    with rocprofv3 are reported only while this digest still matches."""
+    """sha256 over the library's sources and compile flags: HBM byte counts
+    taken with rocprofv3 are reported only while this digest still matches."""
     import hashlib
 
-    csrc = os.path.join(ROOT, "attention_fa_fwd_06_amd", "csrc")
+    from attention_fa_fwd_06_amd import build as fa_build
+
     hsh = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hpp", ".hip", ".cpp", ".h")):
-            hsh.update(name.encode())
-            with open(os.path.join(csrc, name), "rb") as fh:
-                hsh.update(fh.read())
-    with open(os.path.join(ROOT, "attention_fa_fwd_06_amd", "build.py"), "rb") as fh:
-        hsh.update(fh.read())
+    for name in sorted(fa_build.SOURCES) + sorted(
+            n for n in os.listdir(fa_build.CSRC) if n.endswith((".hpp", ".h"))):
+        hsh.update(name.encode())
+        with open(os.path.join(fa_build.CSRC, name), "rb") as fh:
+            hsh.update(fh.read())
+    hsh.update(repr((fa_build.ARCH, fa_build.COMMON)).encode())
     return hsh.hexdigest()
 
 
