@@ -240,6 +240,9 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
     dma.init(lane, w, D);
     float* red = reinterpret_cast<float*>(smem + NS * C::STAGEB);
     const int cb = dw * C::SCH;  // chunk base of this wave's d slice
+    // allowed entries: row - key in [dlo, dhi)
+    const int dlo = a.causal ? 0 : INT_MIN;
+    const int dhi = a.window ? a.window : INT_MAX;
 
     auto issue = [&](int t) {
         char* st = smem + (t % NS) * C::STAGEB;
@@ -261,29 +264,53 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
         const char* kl = smem + (t % NS) * C::STAGEB;
         const char* vl = kl + C::TILEB;
         const int t0 = (t_lo + t) * BKV;
+        // S^T = K Q^T in batches of FB fragments; each batch's K fragments are
+        // requested before the previous batch's MFMAs
         f32x16 s[C::NKB];
+        {
+            constexpr int FB = C::NKG < 8 ? C::NKG : 8, BPK = C::NKG / FB, NB = C::NKB * BPK;
+            auto load = [&](int k, u32x4 (&f)[FB]) {
 #pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) {
-            u32x4 kfr[C::NKG];
+                for (int i = 0; i < FB; ++i) f[i] = ld16(kl + to.natural(32 * (k / BPK), (k % BPK) * FB + i, cb));
+            };
+            u32x4 cur[FB];
+            load(0, cur);
 #pragma unroll
-            for (int gi = 0; gi < C::NKG; ++gi) kfr[gi] = ld16(kl + to.natural(32 * kb, gi, cb));
-            sched_fence();
-            s[kb] = zero16();
+            for (int k = 0; k < NB; ++k) {
+                u32x4 nxt[FB];
+                if (k + 1 < NB) load(k + 1, nxt);
+                sched_fence();
+                const int kb = k / BPK, g0 = (k % BPK) * FB;
+                if (g0 == 0) s[kb] = zero16();
 #pragma unroll
-            for (int gi = 0; gi < C::NKG; ++gi) Mma<T>::nat(s[kb], kfr[gi], qf[gi]);
+                for (int i = 0; i < FB; ++i) Mma<T>::nat(s[kb], cur[i], qf[g0 + i]);
+                sched_fence();
+                if (k + 1 < NB) {
+#pragma unroll
+                    for (int i = 0; i < FB; ++i) cur[i] = nxt[i];
+                }
+            }
         }
         if constexpr (DW > 1) reduce_partials<DW, C::NKB>(s, red, rw * DW, dw, lane);
+
+        // V^T fragments of the first output block, in flight during the softmax
+        u32x4 vcur[C::NPG];
+#pragma unroll
+        for (int gg = 0; gg < C::NPG; ++gg)
+            vcur[gg] = rd_tr(vl + to.transposed(gg, 0, cb, 0), vl + to.transposed(gg, 0, cb, 1));
 
         const bool need = (t0 + BKV > a.Lkv) || (a.causal && t0 + BKV - 1 > i0) ||
                           (a.window && i_last - t0 >= a.window);
         float mx = -INFINITY;
         if (need) {
+            // key j allowed for this row: j < Lkv and row - j in [dlo, dhi)
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int j = t0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-                    if (!(j < a.Lkv && mask_ok(row, j, a.causal, a.window))) s[kb][r] = -INFINITY;
+                    const int j = t0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3), dd = row - j;
+                    const bool ok = (j < a.Lkv) & (dd >= dlo) & (dd < dhi);
+                    s[kb][r] = ok ? s[kb][r] : -INFINITY;
                     mx = fmaxf(mx, s[kb][r]);
                 }
         } else {
@@ -325,18 +352,27 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
         }
         l_run += ls;
 
+        // O^T += V^T P^T, one 32-wide output block at a time; the next block's
+        // fragments are requested before this block's MFMAs
         PF<T> pf[C::NPG];
 #pragma unroll
         for (int gg = 0; gg < C::NPG; ++gg) pf[gg] = make_pf<T>(s[gg >> 1], gg & 1);
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
-            u32x4 vfr[C::NPG];
+            u32x4 vnxt[C::NPG];
+            if (db + 1 < C::NDB) {
 #pragma unroll
-            for (int gg = 0; gg < C::NPG; ++gg)
-                vfr[gg] = rd_tr(vl + to.transposed(gg, db, cb, 0), vl + to.transposed(gg, db, cb, 1));
+                for (int gg = 0; gg < C::NPG; ++gg)
+                    vnxt[gg] = rd_tr(vl + to.transposed(gg, db + 1, cb, 0), vl + to.transposed(gg, db + 1, cb, 1));
+            }
             sched_fence();
 #pragma unroll
-            for (int gg = 0; gg < C::NPG; ++gg) Mma<T>::nat(o[db], vfr[gg], pf[gg].v);
+            for (int gg = 0; gg < C::NPG; ++gg) Mma<T>::nat(o[db], vcur[gg], pf[gg].v);
+            sched_fence();
+            if (db + 1 < C::NDB) {
+#pragma unroll
+                for (int gg = 0; gg < C::NPG; ++gg) vcur[gg] = vnxt[gg];
+            }
         }
     }
 
@@ -431,6 +467,9 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
     dma.init(lane, w, D);
     float* red = reinterpret_cast<float*>(smem + NS * C::STAGEB);
     const int cb = dw * C::SCH;
+    // allowed entries: row - key in [dlo, dhi)
+    const int dlo = a.causal ? 0 : INT_MIN;
+    const int dhi = a.window ? a.window : INT_MAX;
 
     auto issue = [&](int t) {
         char* st = smem + (t % NS) * C::STAGEB;
@@ -452,26 +491,43 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
         const char* kl = smem + (t % NS) * C::STAGEB;
         const char* vl = kl + C::TILEB;
         const int t0 = (t_lo + t) * BKV;
+        // S^T = K Q^T and dP^T = V dO^T in batches of H fragments of each; a
+        // batch's K/V fragments are requested before the previous batch's MFMAs
         f32x16 s[C::NKB], dp[C::NKB];
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) {
-            s[kb] = zero16();
-            dp[kb] = zero16();
-            constexpr int H = C::NKG > 4 ? C::NKG / 2 : C::NKG;  // fragments per batch
-#pragma unroll
-            for (int g0 = 0; g0 < C::NKG; g0 += H) {
-                u32x4 kfr[H], vfr[H];
+        {
+            constexpr int H = 2, BPK = C::NKG / H, NB = C::NKB * BPK;
+            auto load = [&](int k, u32x4 (&kf)[H], u32x4 (&vf)[H]) {
 #pragma unroll
                 for (int i = 0; i < H; ++i) {
-                    const int off = to.natural(32 * kb, g0 + i, cb);
-                    kfr[i] = ld16(kl + off);
-                    vfr[i] = ld16(vl + off);
+                    const int off = to.natural(32 * (k / BPK), (k % BPK) * H + i, cb);
+                    kf[i] = ld16(kl + off);
+                    vf[i] = ld16(vl + off);
+                }
+            };
+            u32x4 kcur[H], vcur[H];
+            load(0, kcur, vcur);
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                u32x4 knxt[H], vnxt[H];
+                if (k + 1 < NB) load(k + 1, knxt, vnxt);
+                sched_fence();
+                const int kb = k / BPK, g0 = (k % BPK) * H;
+                if (g0 == 0) {
+                    s[kb] = zero16();
+                    dp[kb] = zero16();
+                }
+#pragma unroll
+                for (int i = 0; i < H; ++i) {
+                    Mma<T>::nat(s[kb], kcur[i], qf[g0 + i]);
+                    Mma<T>::nat(dp[kb], vcur[i], df[g0 + i]);
                 }
                 sched_fence();
+                if (k + 1 < NB) {
 #pragma unroll
-                for (int i = 0; i < H; ++i) {
-                    Mma<T>::nat(s[kb], kfr[i], qf[g0 + i]);
-                    Mma<T>::nat(dp[kb], vfr[i], df[g0 + i]);
+                    for (int i = 0; i < H; ++i) {
+                        kcur[i] = knxt[i];
+                        vcur[i] = vnxt[i];
+                    }
                 }
             }
         }
@@ -479,31 +535,49 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
             reduce_partials<DW, C::NKB>(s, red, rw * DW, dw, lane);
             reduce_partials<DW, C::NKB>(dp, red + RW * DW * C::NKB * 16 * 64, rw * DW, dw, lane);
         }
+
         const bool need = (t0 + BKV > a.Lkv) || (a.causal && t0 + BKV - 1 > i0) ||
                           (a.window && i_last - t0 >= a.window);
+        auto dscore = [&](auto masked) {
 #pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
+            for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float p = fast_exp2(fmaf(s[kb][r], a.c, -lse2));
-                if (need) {
-                    const int j = t0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-                    if (!(j < a.Lkv && mask_ok(row, j, a.causal, a.window))) p = 0.f;
+                for (int r = 0; r < 16; ++r) {
+                    float p = fast_exp2(fmaf(s[kb][r], a.c, -lse2));
+                    if constexpr (decltype(masked)::value) {
+                        const int j = t0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3), dd = row - j;
+                        p = ((j < a.Lkv) & (dd >= dlo) & (dd < dhi)) ? p : 0.f;
+                    }
+                    s[kb][r] = p * (dp[kb][r] - dl);  // dS^T
                 }
-                s[kb][r] = p * (dp[kb][r] - dl);  // dS^T
-            }
+        };
+        if (need) dscore(std::true_type{});
+        else dscore(std::false_type{});
         PF<T> pf[C::NPG];
 #pragma unroll
         for (int gg = 0; gg < C::NPG; ++gg) pf[gg] = make_pf<T>(s[gg >> 1], gg & 1);
+        // dQ^T += K^T dS^T, one 32-wide output block at a time; the next block's
+        // K^T fragments are requested before this block's MFMAs
+        u32x4 kt[C::NPG];
+#pragma unroll
+        for (int gg = 0; gg < C::NPG; ++gg)
+            kt[gg] = rd_tr(kl + to.transposed(gg, 0, cb, 0), kl + to.transposed(gg, 0, cb, 1));
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
-            u32x4 kfr[C::NPG];
+            u32x4 knxt[C::NPG];
+            if (db + 1 < C::NDB) {
 #pragma unroll
-            for (int gg = 0; gg < C::NPG; ++gg)
-                kfr[gg] = rd_tr(kl + to.transposed(gg, db, cb, 0), kl + to.transposed(gg, db, cb, 1));
+                for (int gg = 0; gg < C::NPG; ++gg)
+                    knxt[gg] = rd_tr(kl + to.transposed(gg, db + 1, cb, 0), kl + to.transposed(gg, db + 1, cb, 1));
+            }
             sched_fence();
 #pragma unroll
-            for (int gg = 0; gg < C::NPG; ++gg) Mma<T>::nat(acc[db], kfr[gg], pf[gg].v);
+            for (int gg = 0; gg < C::NPG; ++gg) Mma<T>::nat(acc[db], kt[gg], pf[gg].v);
+            sched_fence();
+            if (db + 1 < C::NDB) {
+#pragma unroll
+                for (int gg = 0; gg < C::NPG; ++gg) kt[gg] = knxt[gg];
+            }
         }
     }
 
