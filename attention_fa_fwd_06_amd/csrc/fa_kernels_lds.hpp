@@ -91,6 +91,19 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
 // fragment (left alone, the scheduler serialises read -> wait -> MFMA).
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// Issue priority around the MFMA chains of the forward and dQ kernels (two
+// workgroups share a CU there): the wave in its product phase goes first, the
+// other wave's softmax VALU fills the issue slots in between.
+#ifndef FA2_MFMA_PRIO
+#define FA2_MFMA_PRIO 0
+#endif
+__device__ __forceinline__ void prio_mfma() {
+    if constexpr (FA2_MFMA_PRIO) __builtin_amdgcn_s_setprio(1);
+}
+__device__ __forceinline__ void prio_valu() {
+    if constexpr (FA2_MFMA_PRIO) __builtin_amdgcn_s_setprio(0);
+}
+
 template <class T> struct Vec8;
 template <> struct Vec8<__bf16> {
     typedef bf16x8 type;
@@ -275,6 +288,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
             };
             u32x4 cur[FB];
             load(0, cur);
+            prio_mfma();
 #pragma unroll
             for (int k = 0; k < NB; ++k) {
                 u32x4 nxt[FB];
@@ -291,6 +305,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
                 }
             }
         }
+        prio_valu();
         if constexpr (DW > 1) reduce_partials<DW, C::NKB>(s, red, rw * DW, dw, lane);
 
         // V^T fragments of the first output block, in flight during the softmax
@@ -357,6 +372,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
         PF<T> pf[C::NPG];
 #pragma unroll
         for (int gg = 0; gg < C::NPG; ++gg) pf[gg] = make_pf<T>(s[gg >> 1], gg & 1);
+        prio_mfma();
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
             u32x4 vnxt[C::NPG];
@@ -374,6 +390,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
                 for (int gg = 0; gg < C::NPG; ++gg) vcur[gg] = vnxt[gg];
             }
         }
+        prio_valu();
     }
 
     const float l = l_run + __shfl_xor(l_run, 32);
@@ -506,6 +523,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
             };
             u32x4 kcur[H], vcur[H];
             load(0, kcur, vcur);
+            prio_mfma();
 #pragma unroll
             for (int k = 0; k < NB; ++k) {
                 u32x4 knxt[H], vnxt[H];
@@ -531,6 +549,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
                 }
             }
         }
+        prio_valu();
         if constexpr (DW > 1) {
             reduce_partials<DW, C::NKB>(s, red, rw * DW, dw, lane);
             reduce_partials<DW, C::NKB>(dp, red + RW * DW * C::NKB * 16 * 64, rw * DW, dw, lane);
@@ -562,6 +581,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
 #pragma unroll
         for (int gg = 0; gg < C::NPG; ++gg)
             kt[gg] = rd_tr(kl + to.transposed(gg, 0, cb, 0), kl + to.transposed(gg, 0, cb, 1));
+        prio_mfma();
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
             u32x4 knxt[C::NPG];
@@ -579,6 +599,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
                 for (int gg = 0; gg < C::NPG; ++gg) kt[gg] = knxt[gg];
             }
         }
+        prio_valu();
     }
 
     if (row < a.Lq) {
