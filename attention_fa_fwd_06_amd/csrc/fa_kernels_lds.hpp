@@ -862,30 +862,34 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_lds_kernel(BwdArgs a
 // last one down with heads innermost, so the workgroups of a group stream the
 // same Q/dO tiles at about the same time through that XCD's L2.
 // ===========================================================================
-template <class T, int DMAX, int BQ, int KW> struct DkvPipeCfg {
+template <class T, int DMAX, int BQ, int KW, int DW> struct DkvPipeCfg {
     static constexpr int NS = 3;  // tile t (computing), t+1 (landed), t+2 (in flight)
-    static constexpr int NW = 2 * KW, NT = 64 * NW, BKV = 32 * KW;
-    static constexpr int NKG = DMAX / 16, NDB = DMAX / 32;
+    static constexpr int NW = 2 * KW * DW, NT = 64 * NW, BKV = 32 * KW;
+    static constexpr int DS = DMAX / DW;                  // head-dim slice of one wave
+    static constexpr int SCH = DS / 8, NKG = DS / 16, NDB = DS / 32;
     static constexpr int NRB = BQ / 32, NPG = BQ / 16;
     static constexpr int ROWB = DMAX * 2, TILEB = BQ * ROWB;
     static constexpr int ROWSB = 2 * BQ * 4;  // lse and delta of the tile's rows
     static constexpr int STAGEB = 2 * TILEB + ((ROWSB + 1023) / 1024) * 1024;
-    static constexpr int PBUF = KW * NPG * 64 * 16;  // P of every dV wave as MFMA operands, lane-major
-    static constexpr int LDS = NS * STAGEB + 2 * PBUF;
+    static constexpr int PBUF = KW * NPG * 64 * 16;  // P of every key block as MFMA operands, lane-major
+    // partial S / dP of every wave (d split over DW waves), fp32, lane-major
+    static constexpr int XBUF = DW > 1 ? NW * NRB * 16 * 64 * 4 : 0;
+    static constexpr int LDS = NS * STAGEB + 2 * PBUF + XBUF;
     static_assert(LDS <= kLdsBudget, "dK/dV stages do not fit in LDS");
-    static_assert(DMAX % 64 == 0 && (BQ == 32 || BQ == 64), "configuration");
+    static_assert(DS % 64 == 0 && (BQ == 32 || BQ == 64) && (DW == 1 || DW == 2), "configuration");
 };
 
-template <class T, int DMAX, int BQ, int KW, int OCC, int PRIO>
-__global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, int pair) {
-    using C = DkvPipeCfg<T, DMAX, BQ, KW>;
+template <class T, int DMAX, int BQ, int KW, int DW, int OCC, int PRIO>
+__global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, int pair) {
+    using C = DkvPipeCfg<T, DMAX, BQ, KW, DW>;
     using T8 = typename Vec8<T>::type;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: buffer descriptors below depend on it
     const int h = lane >> 5, ln = lane & 31;
-    const bool vw = w < KW;  // dV wave (else dK wave)
-    const int kw = w % KW;
+    const bool vw = w < KW * DW;  // dV wave (else dK wave)
+    const int kw = (w % (KW * DW)) / DW;  // key block of this wave
+    const int dw = w % DW;                // head-dim slice of this wave
     if (PRIO && vw) __builtin_amdgcn_s_setprio(1);
 
     const int nkt = (a.Lkv + C::BKV - 1) / C::BKV;
@@ -913,8 +917,12 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
     to.init(lane);
     DmaPlan<BQ, DMAX, C::NW> dma;
     dma.init(lane, w, D);
-    constexpr int WD = KW;  // delta is fetched by the first dK wave, lse by wave 0
+    constexpr int WD = KW * DW;  // delta is fetched by the first dK wave, lse by wave 0
     char* const pbase = smem + C::NS * C::STAGEB + (kw * C::NPG * 64 + lane) * 16;
+    // partial-sum slots: this wave's, and the wave with the other d slice of the same role and key block
+    f32x4* const xown = reinterpret_cast<f32x4*>(smem + C::NS * C::STAGEB + 2 * C::PBUF) + w * C::NRB * 4 * 64 + lane;
+    const f32x4* const xoth = xown + (DW > 1 ? (dw == 0 ? 1 : -1) : 0) * C::NRB * 4 * 64;
+    const int cb = dw * C::SCH;  // chunk base of this wave's d slice
     // allowed entries: query - key in [dlo, dhi)
     const int dlo = a.causal ? 0 : INT_MIN;
     const int dhi = a.window ? a.window : INT_MAX;
@@ -925,7 +933,7 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
     // same order), so each is register-allocated and scheduled on its own.
     auto run = [&](auto role) {
         constexpr bool V = decltype(role)::value;
-    #pragma unroll 1
+#pragma unroll 1
         for (int pass = 0; pass < 2; ++pass) {
             const int kt = pass ? kt1 : kt0;
             if (kt < 0) break;
@@ -933,13 +941,13 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
             const int key = j0 + 32 * kw + ln;
 
             u32x4 bf[C::NKG];
-    #pragma unroll
+#pragma unroll
             for (int gi = 0; gi < C::NKG; ++gi) {
-                const int c = 2 * gi + h;
+                const int c = cb + 2 * gi + h;
                 bf[gi] = buf_ld16(rkv, c * 8 < D ? (uint32_t)((key * D + c * 8) * 2) : kOob);
             }
             f32x16 acc[C::NDB];  // dV^T (dV wave) or dK^T (dK wave)
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < C::NDB; ++i) acc[i] = zero16();
 
             const int j_last = min(j0 + C::BKV, a.Lkv) - 1;
@@ -982,8 +990,8 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
 
             // row block 0 of the phase-A operand of the tile being computed
             u32x4 fr0[C::NKG];
-    #pragma unroll
-            for (int gi = 0; gi < C::NKG; ++gi) fr0[gi] = ld16(smem + aoff + to.natural(0, gi, 0));
+#pragma unroll
+            for (int gi = 0; gi < C::NKG; ++gi) fr0[gi] = ld16(smem + aoff + to.natural(0, gi, cb));
 
             int slot = 0, qt_cur = qt_hi, hq_cnt = 0;
             for (int it = 0; it < n_it; ++it) {
@@ -1003,34 +1011,56 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
                     constexpr int HG = C::NKG / 2;
                     u32x4 fr1[C::NKG];
                     if constexpr (C::NRB == 2) {
-    #pragma unroll
-                        for (int gi = 0; gi < HG; ++gi) fr1[gi] = ld16(st + aoff + to.natural(32, gi, 0));
+#pragma unroll
+                        for (int gi = 0; gi < HG; ++gi) fr1[gi] = ld16(st + aoff + to.natural(32, gi, cb));
                     }
                     sched_fence();
                     x[0] = zero16();
-    #pragma unroll
+#pragma unroll
                     for (int gi = 0; gi < C::NKG; ++gi) Mma<T>::nat(x[0], fr0[gi], bf[gi]);
                     sched_fence();
                     if constexpr (C::NRB == 2) {
-    #pragma unroll
-                        for (int gi = HG; gi < C::NKG; ++gi) fr1[gi] = ld16(st + aoff + to.natural(32, gi, 0));
+#pragma unroll
+                        for (int gi = HG; gi < C::NKG; ++gi) fr1[gi] = ld16(st + aoff + to.natural(32, gi, cb));
                     }
-    #pragma unroll
+#pragma unroll
                     for (int db = 0; db < C::NDB; ++db)
-                        nx[db] = rd_tr(tb + to.transposed(0, db, 0, 0), tb + to.transposed(0, db, 0, 1));
+                        nx[db] = rd_tr(tb + to.transposed(0, db, cb, 0), tb + to.transposed(0, db, cb, 1));
                     sched_fence();
                     if constexpr (C::NRB == 2) {
                         x[1] = zero16();
-    #pragma unroll
+#pragma unroll
                         for (int gi = 0; gi < C::NKG; ++gi) Mma<T>::nat(x[1], fr1[gi], bf[gi]);
                     }
                     sched_fence();
                     const float* rowv = lf + (V ? 0 : BQ) + 4 * h;
-    #pragma unroll
+#pragma unroll
                     for (int rb = 0; rb < C::NRB; ++rb)
-    #pragma unroll
+#pragma unroll
                         for (int qd = 0; qd < 4; ++qd)
                             rv[rb][qd] = *reinterpret_cast<const f32x4*>(rowv + 32 * rb + 8 * qd);
+                }
+                if constexpr (DW > 1) {
+                    // S (or dP) = sum of the two d slices' partial products, added in
+                    // the same order by both waves, so both hold identical bits
+#pragma unroll
+                    for (int rb = 0; rb < C::NRB; ++rb)
+#pragma unroll
+                        for (int qd = 0; qd < 4; ++qd)
+                            xown[(rb * 4 + qd) * 64] = f32x4{x[rb][4 * qd], x[rb][4 * qd + 1], x[rb][4 * qd + 2],
+                                                             x[rb][4 * qd + 3]};
+                    lds_barrier();  // partials visible
+#pragma unroll
+                    for (int rb = 0; rb < C::NRB; ++rb)
+#pragma unroll
+                        for (int qd = 0; qd < 4; ++qd) {
+                            const f32x4 o = xoth[(rb * 4 + qd) * 64];
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const float mine = x[rb][4 * qd + i];
+                                x[rb][4 * qd + i] = dw == 0 ? mine + o[i] : o[i] + mine;
+                            }
+                        }
                 }
 
                 PF<T> pf[C::NPG];
@@ -1038,9 +1068,9 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
                     // P = exp2(c S - log2(e) lse), masked entries 0; x[rb][4 qd + i] is
                     // row 32 rb + 8 qd + 4 h + i of the tile
                     auto probs = [&](auto masked) {
-    #pragma unroll
+#pragma unroll
                         for (int rb = 0; rb < C::NRB; ++rb)
-    #pragma unroll
+#pragma unroll
                             for (int r = 0; r < 16; ++r) {
                                 float p = fast_exp2(fmaf(x[rb][r], a.c, -rv[rb][r >> 2][r & 3] * kLog2e));
                                 if constexpr (decltype(masked)::value) {
@@ -1054,16 +1084,16 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
                                       (a.window && min(q0 + BQ, a.Lq) - 1 - j0 >= a.window);
                     if (need) probs(std::true_type{});
                     else probs(std::false_type{});
-    #pragma unroll
+#pragma unroll
                     for (int gg = 0; gg < C::NPG; ++gg) {
                         pf[gg] = make_pf<T>(x[gg >> 1], gg & 1);
-                        st16(pb + gg * 1024, pf[gg].v);
+                        if (DW == 1 || dw == 0) st16(pb + gg * 1024, pf[gg].v);
                     }
                 } else {
                     // dP - Delta while the dV wave is still on its exp phase
-    #pragma unroll
+#pragma unroll
                     for (int rb = 0; rb < C::NRB; ++rb)
-    #pragma unroll
+#pragma unroll
                         for (int r = 0; r < 16; ++r) x[rb][r] -= rv[rb][r >> 2][r & 3];
                 }
                 wait_vm<0>();   // this wave's share of tile it+1
@@ -1080,7 +1110,7 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
                 auto ds_group = [&](int gg) {
                     const T8 pv = __builtin_bit_cast(T8, ld16(pb + gg * 1024));
                     const int rb = gg >> 1, hf = gg & 1;
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < 8; ++i) {
                         const int r = 8 * hf + i;
                         x[rb][r] *= (float)pv[i];
@@ -1088,27 +1118,27 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
                     pf[gg] = make_pf<T>(x[rb], hf);
                 };
                 if constexpr (!V) ds_group(0);
-    #pragma unroll
+#pragma unroll
                 for (int gg = 0; gg < C::NPG; ++gg) {
                     u32x4 nn[C::NDB];
                     if (gg + 1 < C::NPG) {
-    #pragma unroll
+#pragma unroll
                         for (int db = 0; db < C::NDB; ++db)
-                            nn[db] = rd_tr(tb + to.transposed(gg + 1, db, 0, 0), tb + to.transposed(gg + 1, db, 0, 1));
+                            nn[db] = rd_tr(tb + to.transposed(gg + 1, db, cb, 0), tb + to.transposed(gg + 1, db, cb, 1));
                     } else {
                         const char* an = smem + nslot * C::STAGEB + aoff;
-    #pragma unroll
-                        for (int gi = 0; gi < C::NKG; ++gi) fr0[gi] = ld16(an + to.natural(0, gi, 0));
+#pragma unroll
+                        for (int gi = 0; gi < C::NKG; ++gi) fr0[gi] = ld16(an + to.natural(0, gi, cb));
                     }
                     sched_fence();
-    #pragma unroll
+#pragma unroll
                     for (int db = 0; db < C::NDB; ++db) Mma<T>::nat(acc[db], nx[db], pf[gg].v);
                     if constexpr (!V) {
                         if (gg + 1 < C::NPG) ds_group(gg + 1);
                     }
                     sched_fence();
                     if (gg + 1 < C::NPG) {
-    #pragma unroll
+#pragma unroll
                         for (int db = 0; db < C::NDB; ++db) nx[db] = nn[db];
                     }
                 }
@@ -1122,11 +1152,11 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
             if (key < a.Lkv) {
                 T* op = reinterpret_cast<T*>(V ? a.dv : a.dk) + kvhead + (size_t)key * D;
                 const float sc = V ? 1.f : a.scale;
-    #pragma unroll
+#pragma unroll
                 for (int db = 0; db < C::NDB; ++db)
-    #pragma unroll
+#pragma unroll
                     for (int qd = 0; qd < 4; ++qd) {
-                        const int d = 32 * db + 8 * qd + 4 * h;
+                        const int d = dw * C::DS + 32 * db + 8 * qd + 4 * h;
                         if (d < D)
                             store4<T>(op + d, acc[db][4 * qd] * sc, acc[db][4 * qd + 1] * sc,
                                       acc[db][4 * qd + 2] * sc, acc[db][4 * qd + 3] * sc);
@@ -1176,10 +1206,10 @@ hipError_t launch_dkv2(const BwdArgs& a, hipStream_t s) {
 // without window; it is used only while it still leaves a workgroup for each
 // of the 256 CUs.
 constexpr int kPairMinGrid = 256;
-template <class T, int DMAX, int BQ, int KW, int OCC, int PRIO>
+template <class T, int DMAX, int BQ, int KW, int DW, int OCC, int PRIO>
 hipError_t launch_dkv_pipe(const BwdArgs& a, hipStream_t s) {
-    using C = DkvPipeCfg<T, DMAX, BQ, KW>;
-    auto kern = fa_dkv_pipe_kernel<T, DMAX, BQ, KW, OCC, PRIO>;
+    using C = DkvPipeCfg<T, DMAX, BQ, KW, DW>;
+    auto kern = fa_dkv_pipe_kernel<T, DMAX, BQ, KW, DW, OCC, PRIO>;
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
     const long long nkt = (a.Lkv + C::BKV - 1) / C::BKV;
@@ -1244,18 +1274,22 @@ template <class T> hipError_t launch_dq16(const BwdArgs& a, hipStream_t s) {
         default: return launch_dq2<T, 512, FA2_DQ_512>(a, s);
     }
 }
-// dK/dV on wave pairs: <query tile, key blocks of 32, min waves per SIMD, dV-wave priority>.
+// dK/dV on wave pairs: <query tile, key blocks of 32, waves splitting d, min waves per SIMD,
+// dV-wave priority>.
 #ifndef FA2_DKVS_64
-#define FA2_DKVS_64 64, 4, 2, 1
+#define FA2_DKVS_64 64, 4, 1, 2, 1
 #endif
 #ifndef FA2_DKVS_128
-#define FA2_DKVS_128 64, 4, 2, 1
+#define FA2_DKVS_128 64, 4, 1, 2, 1
+#endif
+#ifndef FA2_DKVS_256
+#define FA2_DKVS_256 32, 2, 2, 2, 1
 #endif
 template <class T> hipError_t launch_dkv16(const BwdArgs& a, hipStream_t s) {
     switch (dmax16(a.D)) {
         case 64: return launch_dkv_pipe<T, 64, FA2_DKVS_64>(a, s);
         case 128: return launch_dkv_pipe<T, 128, FA2_DKVS_128>(a, s);
-        case 256: return launch_dkv2<T, 256, FA2_DKV_256>(a, s);
+        case 256: return launch_dkv_pipe<T, 256, FA2_DKVS_256>(a, s);
         default: return launch_dkv2<T, 512, FA2_DKV_512>(a, s);
     }
 }

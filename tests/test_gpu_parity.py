@@ -153,6 +153,11 @@ SWEEP = [
     (1, 4, 2, 64, 200, 128, "bf16", False, 0),
     (2, 4, 1, 50, 90, 32, "f32", False, 0),
     (1, 16, 16, 17, 17, 64, "bf16", False, 0),
+    # d split over two waves in dK/dV (head dims 136..256): window, ragged, Lq != Lkv
+    (1, 4, 1, 333, 333, 256, "bf16", True, 100),
+    (1, 2, 2, 150, 260, 248, "f16", True, 40),
+    (1, 8, 2, 96, 96, 256, "f16", True, 0),
+    (2, 2, 1, 70, 45, 136, "bf16", False, 0),
 ]
 
 
