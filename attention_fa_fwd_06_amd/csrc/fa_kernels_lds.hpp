@@ -1234,7 +1234,7 @@ inline int dmax16(int D) { return D <= 64 ? 64 : D <= 128 ? 128 : D <= 256 ? 256
 #define FA2_FWD_128 64, 4, 1, 2, 2
 #endif
 #ifndef FA2_FWD_256
-#define FA2_FWD_256 64, 4, 1, 1, 2
+#define FA2_FWD_256 32, 2, 2, 2, 2
 #endif
 #ifndef FA2_FWD_512
 #define FA2_FWD_512 32, 1, 4, 1, 2
@@ -1283,7 +1283,7 @@ template <class T> hipError_t launch_dq16(const BwdArgs& a, hipStream_t s) {
 #define FA2_DKVS_128 64, 4, 1, 2, 1
 #endif
 #ifndef FA2_DKVS_256
-#define FA2_DKVS_256 32, 2, 2, 2, 1
+#define FA2_DKVS_256 32, 2, 2, 2, 0
 #endif
 template <class T> hipError_t launch_dkv16(const BwdArgs& a, hipStream_t s) {
     switch (dmax16(a.D)) {
