@@ -1251,9 +1251,6 @@ inline int dmax16(int D) { return D <= 64 ? 64 : D <= 128 ? 128 : D <= 256 ? 256
 #ifndef FA2_DQ_512
 #define FA2_DQ_512 32, 1, 4, 1, 2
 #endif
-#ifndef FA2_DKV_256
-#define FA2_DKV_256 32, 2, 2, 1, 2
-#endif
 #ifndef FA2_DKV_512
 #define FA2_DKV_512 32, 1, 4, 1, 2
 #endif

@@ -29,6 +29,12 @@ Sources (the pages this follows):
     dK += ds q scale, dQ += ds k scale.
   * ggmlR R/ag_flash_attn.R, `.ag_flash_mask`: causal means query j attends to
     keys 1..j (top-left alignment).
+  * ggmlR R/ag_flash_attn.R, `ag_flash_attention` (`mask` argument) and
+    `.ag_flash_mask`: an optional numeric mask per (query, key), 0 to attend
+    and -Inf to block, the same mask for the forward and the gradient. Here
+    it is the `bias` argument, indexed [.., query, key]; a finite value is
+    added to the scaled score (the reading under which 0 leaves a score alone
+    and -Inf removes it), and it carries no gradient.
 
 Readings where the pages are silent or disagree (each listed in the design notes):
   * a row whose every key is masked gets O = 0, LSE = -inf and contributes no
@@ -76,13 +82,15 @@ def _kv_head(h: int, Hq: int, Hkv: int) -> int:
     return h // (Hq // Hkv)
 
 
-def rows_forward(q_rows, K, V, rows, scale, causal, window, cols=None):
+def rows_forward(q_rows, K, V, rows, scale, causal, window, cols=None, bias_rows=None):
     """Forward for a set of query rows of one (b, h).
 
     q_rows [R, D], K and V [Lkv, D], rows = the R absolute row indices.
     cols (optional) = absolute key indices to evaluate; it must contain every
     allowed key of every row, and then the result is exact, because masked
     probabilities are exactly 0 (the returned S and P cover only cols).
+    bias_rows (optional) [R, Lkv]: additive mask of these rows over all keys
+    (finite or -inf), added to the scaled scores.
     Returns S (masked, -inf where forbidden), P, O [R, D], LSE [R].
     """
     q_rows = np.asarray(q_rows, dtype=np.float64)
@@ -94,6 +102,12 @@ def rows_forward(q_rows, K, V, rows, scale, causal, window, cols=None):
         Kc, Vc = K[cols], V[cols]
     S = scale * (q_rows @ Kc.T)
     ok = mask_matrix(rows, K.shape[0], causal, window, cols=cols)
+    if bias_rows is not None:
+        bias = np.asarray(bias_rows, dtype=np.float64)[:, cols]
+        if np.isnan(bias).any() or np.isposinf(bias).any():
+            raise ValueError("mask values must be finite or -inf")
+        ok = ok & np.isfinite(bias)
+        S = S + np.where(np.isfinite(bias), bias, 0.0)
     S = np.where(ok, S, -np.inf)
     m = S.max(axis=1)
     live = np.isfinite(m)
@@ -117,17 +131,28 @@ def key_span(rows, Lkv, causal, window):
     return np.arange(lo, hi + 1) if hi >= lo else np.arange(0)
 
 
-def forward(q, k, v, scale, causal=False, window=0):
-    """O [B,Hq,Lq,D] and natural-log LSE [B,Hq,Lq] for float64 inputs."""
+def _bias(bias, B, Hq, Lq, Lkv):
+    """The additive mask broadcast to [B, Hq, Lq, Lkv], or None."""
+    if bias is None:
+        return None
+    return np.broadcast_to(np.asarray(bias, dtype=np.float64), (B, Hq, Lq, Lkv))
+
+
+def forward(q, k, v, scale, causal=False, window=0, bias=None):
+    """O [B,Hq,Lq,D] and natural-log LSE [B,Hq,Lq] for float64 inputs.
+
+    bias: optional additive mask broadcastable to [B, Hq, Lq, Lkv]."""
     B, Hq, Lq, D = q.shape
     Hkv = k.shape[1]
+    bias = _bias(bias, B, Hq, Lq, k.shape[2])
     O = np.zeros((B, Hq, Lq, v.shape[3]))
     LSE = np.zeros((B, Hq, Lq))
     rows = np.arange(Lq)
     for b in range(B):
         for h in range(Hq):
             g = _kv_head(h, Hq, Hkv)
-            _, _, O[b, h], LSE[b, h] = rows_forward(q[b, h], k[b, g], v[b, g], rows, scale, causal, window)
+            _, _, O[b, h], LSE[b, h] = rows_forward(q[b, h], k[b, g], v[b, g], rows, scale, causal, window,
+                                                    bias_rows=None if bias is None else bias[b, h])
     return O, LSE
 
 
@@ -136,13 +161,15 @@ def bwd_preprocess(o, do):
     return (np.asarray(do, dtype=np.float64) * np.asarray(o, dtype=np.float64)).sum(axis=-1)
 
 
-def backward(q, k, v, do, scale, causal=False, window=0):
+def backward(q, k, v, do, scale, causal=False, window=0, bias=None):
     """Gradients of f = sum(dO * O) with respect to q, k, v.
 
+    bias: optional additive mask broadcastable to [B, Hq, Lq, Lkv] (no gradient).
     Returns dict with O, LSE, Delta, dQ, dK, dV (all float64).
     """
     B, Hq, Lq, D = q.shape
     Hkv, Lkv = k.shape[1], k.shape[2]
+    bias = _bias(bias, B, Hq, Lq, Lkv)
     O = np.zeros((B, Hq, Lq, v.shape[3]))
     LSE = np.zeros((B, Hq, Lq))
     Delta = np.zeros((B, Hq, Lq))
@@ -154,7 +181,8 @@ def backward(q, k, v, do, scale, causal=False, window=0):
         for h in range(Hq):  # heads of one group summed in increasing h
             g = _kv_head(h, Hq, Hkv)
             Kg, Vg = k[b, g], v[b, g]
-            _, P, Oh, lse = rows_forward(q[b, h], Kg, Vg, rows, scale, causal, window)
+            _, P, Oh, lse = rows_forward(q[b, h], Kg, Vg, rows, scale, causal, window,
+                                         bias_rows=None if bias is None else bias[b, h])
             dOh = do[b, h]
             dP = dOh @ Vg.T
             delta = bwd_preprocess(Oh, dOh)
