@@ -11,9 +11,15 @@ caller-allocated tensors):
     fa_bwd_preprocess(o, do, delta)
     fa_bwd_dkv(q, k, v, do, lse, delta, dk, dv, scale, causal, window)
     fa_bwd_dq(q, k, v, do, lse, delta, dq, scale, causal, window)
+    fa_fwd_masked, fa_bwd_dkv_masked, fa_bwd_dq_masked: the same with an
+    additive float32 mask tensor after v (resp. delta)
 Convenience wrappers that allocate their outputs:
-    forward(q, k, v, scale=None, causal=False, window=0) -> (o, lse)
-    backward(q, k, v, o, lse, do, scale=None, causal=False, window=0) -> (dq, dk, dv)
+    forward(q, k, v, scale=None, causal=False, window=0, mask=None) -> (o, lse)
+    backward(q, k, v, o, lse, do, scale=None, causal=False, window=0, mask=None) -> (dq, dk, dv)
+A mask is a float32 GPU tensor whose last two dims are [Lq, Lkv] (contiguous
+rows); up to two leading dims broadcast against [B, Hq] the way torch aligns
+shapes (right-aligned, size 1 or the full size). It is added to the scaled
+scores (0 attends, -inf blocks).
 """
 from __future__ import annotations
 
@@ -36,7 +42,8 @@ STATUS = {
     -6: "FA_ERR_ARG",
     -7: "FA_ERR_LAUNCH",
 }
-EXPORTS = ("fa_fwd", "fa_bwd_preprocess", "fa_bwd_dkv", "fa_bwd_dq", "fa_status_string")
+EXPORTS = ("fa_fwd", "fa_bwd_preprocess", "fa_bwd_dkv", "fa_bwd_dq", "fa_fwd_masked", "fa_bwd_dkv_masked",
+           "fa_bwd_dq_masked", "fa_status_string")
 
 _lib = None
 
@@ -62,7 +69,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_preprocess.argtypes = [P, P, P, I, I, I, I, I, P]
     lib.fa_bwd_dkv.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, P]
     lib.fa_bwd_dq.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, P]
-    for fn in ("fa_fwd", "fa_bwd_preprocess", "fa_bwd_dkv", "fa_bwd_dq"):
+    LL = ctypes.c_longlong
+    lib.fa_fwd_masked.argtypes = [P, P, P, P, LL, LL, P, P, I, I, I, I, I, I, F, I, I, I, P]
+    lib.fa_bwd_dkv_masked.argtypes = [P, P, P, P, P, P, P, LL, LL, P, P, I, I, I, I, I, I, F, I, I, I, P]
+    lib.fa_bwd_dq_masked.argtypes = [P, P, P, P, P, P, P, LL, LL, P, I, I, I, I, I, I, F, I, I, I, P]
+    for fn in ("fa_fwd", "fa_bwd_preprocess", "fa_bwd_dkv", "fa_bwd_dq", "fa_fwd_masked", "fa_bwd_dkv_masked",
+               "fa_bwd_dq_masked"):
         getattr(lib, fn).restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -128,8 +140,31 @@ def _attn_shapes(q, k, v):
     return B, Hq, Hkv, Lq, Lkv, D
 
 
-def fa_fwd(q, k, v, o, lse, scale, causal=False, window=0):
-    """O and LSE of softmax attention (see include/fa.h, fa_fwd)."""
+def _mask_args(mask, B, Hq, Lq, Lkv, dev):
+    """(pointer, batch stride, head stride) of an additive float32 mask tensor
+    broadcast to [B, Hq, Lq, Lkv] (see include/fa.h, masked variants)."""
+    import torch
+
+    if not mask.is_cuda or mask.device != dev:
+        raise ValueError(f"mask must be on {dev}")
+    if mask.dtype != torch.float32:
+        raise ValueError(f"mask must be float32, got {mask.dtype}")
+    if mask.dim() < 2 or mask.dim() > 4 or tuple(mask.shape[-2:]) != (Lq, Lkv):
+        raise ValueError(f"mask shape {tuple(mask.shape)} must end in [Lq, Lkv] = [{Lq}, {Lkv}] with at most 4 dims")
+    if mask.stride(-1) != 1 or (Lq > 1 and mask.stride(-2) != Lkv):
+        raise ValueError("mask rows must be contiguous: strides [..., Lkv, 1]")
+    lead = [1] * (4 - mask.dim()) + list(mask.shape[:-2])
+    strides = [0] * (4 - mask.dim()) + list(mask.stride()[:-2])
+    for n, (size, full, name) in enumerate(zip(lead, (B, Hq), ("batch", "head"))):
+        if size not in (1, full):
+            raise ValueError(f"mask {name} dim is {size}; it must be 1 or {full}")
+    msb = strides[0] if lead[0] > 1 else 0
+    msh = strides[1] if lead[1] > 1 else 0
+    return mask.data_ptr(), int(msb), int(msh)
+
+
+def fa_fwd(q, k, v, o, lse, scale, causal=False, window=0, mask=None):
+    """O and LSE of softmax attention (see include/fa.h, fa_fwd / fa_fwd_masked)."""
     lib = load_library()
     B, Hq, Hkv, Lq, Lkv, D = _attn_shapes(q, k, v)
     import torch
@@ -137,10 +172,13 @@ def fa_fwd(q, k, v, o, lse, scale, causal=False, window=0):
     dev, dt = q.device, q.dtype
     if tuple(o.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, Lq):
         raise ValueError("o must match q and lse must be [B, Hq, Lq]")
-    st = lib.fa_fwd(_ptr(q, "q", dev, dt), _ptr(k, "k", dev, dt), _ptr(v, "v", dev, dt), _ptr(o, "o", dev, dt),
-                    _ptr(lse, "lse", dev, torch.float32), B, Hq, Hkv, Lq, Lkv, D, float(scale), int(bool(causal)),
-                    int(window), _dtype_code(q), _stream(dev))
-    _check("fa_fwd", st)
+    ins = (_ptr(q, "q", dev, dt), _ptr(k, "k", dev, dt), _ptr(v, "v", dev, dt))
+    outs = (_ptr(o, "o", dev, dt), _ptr(lse, "lse", dev, torch.float32))
+    rest = (B, Hq, Hkv, Lq, Lkv, D, float(scale), int(bool(causal)), int(window), _dtype_code(q), _stream(dev))
+    if mask is None:
+        _check("fa_fwd", lib.fa_fwd(*ins, *outs, *rest))
+    else:
+        _check("fa_fwd_masked", lib.fa_fwd_masked(*ins, *_mask_args(mask, B, Hq, Lq, Lkv, dev), *outs, *rest))
 
 
 def fa_bwd_preprocess(o, do, delta):
@@ -171,45 +209,54 @@ def _bwd_common(q, k, v, do, lse, delta):
     return (B, Hq, Hkv, Lq, Lkv, D), ptrs, dev, dt
 
 
-def fa_bwd_dkv(q, k, v, do, lse, delta, dk, dv, scale, causal=False, window=0):
-    """dK and dV (see include/fa.h, fa_bwd_dkv)."""
+def fa_bwd_dkv(q, k, v, do, lse, delta, dk, dv, scale, causal=False, window=0, mask=None):
+    """dK and dV (see include/fa.h, fa_bwd_dkv / fa_bwd_dkv_masked)."""
     lib = load_library()
     dims, ptrs, dev, dt = _bwd_common(q, k, v, do, lse, delta)
     if tuple(dk.shape) != tuple(k.shape) or tuple(dv.shape) != tuple(k.shape):
         raise ValueError("dk and dv must match k")
-    st = lib.fa_bwd_dkv(*ptrs, _ptr(dk, "dk", dev, dt), _ptr(dv, "dv", dev, dt), *dims, float(scale),
-                        int(bool(causal)), int(window), _dtype_code(q), _stream(dev))
-    _check("fa_bwd_dkv", st)
+    outs = (_ptr(dk, "dk", dev, dt), _ptr(dv, "dv", dev, dt))
+    rest = (*dims, float(scale), int(bool(causal)), int(window), _dtype_code(q), _stream(dev))
+    if mask is None:
+        _check("fa_bwd_dkv", lib.fa_bwd_dkv(*ptrs, *outs, *rest))
+    else:
+        B, Hq, _, Lq, Lkv, _ = dims
+        margs = _mask_args(mask, B, Hq, Lq, Lkv, dev)
+        _check("fa_bwd_dkv_masked", lib.fa_bwd_dkv_masked(*ptrs, *margs, *outs, *rest))
 
 
-def fa_bwd_dq(q, k, v, do, lse, delta, dq, scale, causal=False, window=0):
-    """dQ (see include/fa.h, fa_bwd_dq)."""
+def fa_bwd_dq(q, k, v, do, lse, delta, dq, scale, causal=False, window=0, mask=None):
+    """dQ (see include/fa.h, fa_bwd_dq / fa_bwd_dq_masked)."""
     lib = load_library()
     dims, ptrs, dev, dt = _bwd_common(q, k, v, do, lse, delta)
     if tuple(dq.shape) != tuple(q.shape):
         raise ValueError("dq must match q")
-    st = lib.fa_bwd_dq(*ptrs, _ptr(dq, "dq", dev, dt), *dims, float(scale), int(bool(causal)), int(window),
-                       _dtype_code(q), _stream(dev))
-    _check("fa_bwd_dq", st)
+    rest = (*dims, float(scale), int(bool(causal)), int(window), _dtype_code(q), _stream(dev))
+    if mask is None:
+        _check("fa_bwd_dq", lib.fa_bwd_dq(*ptrs, _ptr(dq, "dq", dev, dt), *rest))
+    else:
+        B, Hq, _, Lq, Lkv, _ = dims
+        margs = _mask_args(mask, B, Hq, Lq, Lkv, dev)
+        _check("fa_bwd_dq_masked", lib.fa_bwd_dq_masked(*ptrs, *margs, _ptr(dq, "dq", dev, dt), *rest))
 
 
 def default_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)
 
 
-def forward(q, k, v, scale=None, causal=False, window=0):
-    """Allocate O and LSE and run fa_fwd. Returns (o, lse)."""
+def forward(q, k, v, scale=None, causal=False, window=0, mask=None):
+    """Allocate O and LSE and run fa_fwd (fa_fwd_masked with a mask). Returns (o, lse)."""
     import torch
 
     B, Hq, Lq, D = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, Lq), device=q.device, dtype=torch.float32)
-    fa_fwd(q, k, v, o, lse, default_scale(D) if scale is None else scale, causal, window)
+    fa_fwd(q, k, v, o, lse, default_scale(D) if scale is None else scale, causal, window, mask)
     return o, lse
 
 
-def backward(q, k, v, o, lse, do, scale=None, causal=False, window=0, delta=None):
-    """Run the three backward phases. Returns (dq, dk, dv)."""
+def backward(q, k, v, o, lse, do, scale=None, causal=False, window=0, delta=None, mask=None):
+    """Run the three backward phases (masked dK/dV and dQ with a mask). Returns (dq, dk, dv)."""
     import torch
 
     B, Hq, Lq, D = q.shape
@@ -218,6 +265,6 @@ def backward(q, k, v, o, lse, do, scale=None, causal=False, window=0, delta=None
         delta = torch.empty((B, Hq, Lq), device=q.device, dtype=torch.float32)
     fa_bwd_preprocess(o, do, delta)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    fa_bwd_dkv(q, k, v, do, lse, delta, dk, dv, scale, causal, window)
-    fa_bwd_dq(q, k, v, do, lse, delta, dq, scale, causal, window)
+    fa_bwd_dkv(q, k, v, do, lse, delta, dk, dv, scale, causal, window, mask)
+    fa_bwd_dq(q, k, v, do, lse, delta, dq, scale, causal, window, mask)
     return dq, dk, dv

@@ -63,10 +63,11 @@ class FlashAttention(torch.autograd.Function):
     """O, LSE = attention(q, k, v); gradients flow to q, k and v through O."""
 
     @staticmethod
-    def forward(ctx, q, k, v, scale: float, causal: bool, window: int):
+    def forward(ctx, q, k, v, scale: float, causal: bool, window: int, mask=None):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        o, lse = forward(q, k, v, scale, causal, window)
+        o, lse = forward(q, k, v, scale, causal, window, mask=mask)
         ctx.save_for_backward(q, k, v, o, lse)
+        ctx.mask = mask  # the same mask for the gradient; it gets none itself
         ctx.attn = (scale, bool(causal), int(window))
         ctx.mark_non_differentiable(lse)
         return o, lse
@@ -76,13 +77,13 @@ class FlashAttention(torch.autograd.Function):
         q, k, v, o, lse = ctx.saved_tensors
         scale, causal, window = ctx.attn
         if do is None:
-            return None, None, None, None, None, None
-        dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), scale, causal, window)
-        return dq, dk, dv, None, None, None
+            return None, None, None, None, None, None, None
+        dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), scale, causal, window, mask=ctx.mask)
+        return dq, dk, dv, None, None, None, None
 
 
 def flash_attention(q, k, v, scale: float | None = None, causal: bool = False, window: int = 0,
-                    return_lse: bool = False):
+                    return_lse: bool = False, mask=None):
     """Differentiable softmax(scale * q k^T + mask) v on the HIP kernels.
 
     q: [B, Hq, Lq, D]; k, v: [B, Hkv, Lkv, D] (Hq a multiple of Hkv); one of
@@ -90,15 +91,20 @@ def flash_attention(q, k, v, scale: float | None = None, causal: bool = False, w
     causal: key j is allowed for query i only if j <= i (top-left aligned).
     window > 0: additionally only keys with i - j < window (plus, without
     causal, every key after i). Returns O (and the natural-log LSE, which
-    carries no gradient, when return_lse). Raises ValueError for inputs the
-    kernels do not support; nothing is computed any other way.
+    carries no gradient, when return_lse). mask (optional): float32 additive
+    mask [.., Lq, Lkv] added to the scaled scores (0 attends, -inf blocks; see
+    include/fa.h), the same for the gradient, itself without gradient.
+    Raises ValueError for inputs the kernels do not support; nothing is
+    computed any other way.
     """
     reason = unsupported_reason(q, k, v, window)
     if reason is not None:
         raise ValueError(f"flash_attention: {reason}")
     if scale is None:
         scale = default_scale(q.shape[-1])
-    o, lse = FlashAttention.apply(q, k, v, float(scale), bool(causal), int(window))
+    if mask is not None and mask.requires_grad:
+        raise ValueError("flash_attention: the mask carries no gradient; pass mask.detach()")
+    o, lse = FlashAttention.apply(q, k, v, float(scale), bool(causal), int(window), mask)
     return (o, lse) if return_lse else o
 
 

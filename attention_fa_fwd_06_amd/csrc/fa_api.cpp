@@ -45,6 +45,21 @@ fa_status_t check_attn(int B, int Hq, int Hkv, int Lq, int Lkv, int D, float sca
 
 fa_status_t from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
 
+// Mask tensor of the masked entry points: non-NULL, 4-byte aligned, strides
+// in [0, 2^40] elements (far from any overflow of the 64-bit offsets).
+constexpr long long kMaxMaskStride = 1LL << 40;
+fa_status_t check_mask(const float* mask, long long msb, long long msh) {
+    if (!mask) return FA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(mask) & 3u) != 0) return FA_ERR_ALIGN;
+    if (msb < 0 || msh < 0 || msb > kMaxMaskStride || msh > kMaxMaskStride) return FA_ERR_ARG;
+    return FA_OK;
+}
+// 16-byte loads of four consecutive keys are possible when every row of every
+// (batch, head) slice starts 16-byte aligned.
+int mask_vec4(const float* mask, long long msb, long long msh, int Lkv) {
+    return aligned16(mask) && msb % 4 == 0 && msh % 4 == 0 && Lkv % 4 == 0;
+}
+
 // A window of Lq or more keys never masks anything (i - j <= Lq - 1 for every
 // pair), so it is the same as no window; folding it to 0 also keeps the
 // kernels' tile-range arithmetic far from int overflow.
@@ -62,14 +77,15 @@ const char* fa_status_string(fa_status_t s) {
         case FA_ERR_HEADDIM: return "head dim must be a multiple of 8 in [32, 512] ([32, 256] for FA_F32)";
         case FA_ERR_DTYPE: return "unsupported dtype (FA_F32, FA_F16 or FA_BF16)";
         case FA_ERR_ALIGN: return "every pointer must be 16-byte aligned";
-        case FA_ERR_ARG: return "window must be >= 0 and scale finite";
+        case FA_ERR_ARG: return "window must be >= 0, scale finite and mask strides in [0, 2^40]";
         case FA_ERR_LAUNCH: return "HIP kernel launch failed";
     }
     return "unknown status";
 }
 
-fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
-                   int Lq, int Lkv, int D, float scale, int causal, int window, fa_dtype_t dtype, void* stream) {
+static fa_status_t fwd_impl(const void* q, const void* k, const void* v, const float* mask, long long msb,
+                            long long msh, void* o, float* lse, int B, int Hq, int Hkv, int Lq, int Lkv, int D,
+                            float scale, int causal, int window, fa_dtype_t dtype, void* stream) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     fa_status_t st = check_dtype(dtype);
     if (st != FA_OK) return st;
@@ -78,7 +94,8 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
 
     fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Lq, Lkv, D,
-                  (float)((double)scale * 1.4426950408889634), causal ? 1 : 0, effective_window(window, Lq)};
+                  (float)((double)scale * 1.4426950408889634), causal ? 1 : 0, effective_window(window, Lq),
+                  mask, msb, msh, mask ? mask_vec4(mask, msb, msh, Lkv) : 0};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     switch (dtype) {
         case FA_F32: return from_hip(fa::launch_fwd_f32(a, s));
@@ -86,6 +103,20 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
         case FA_BF16: return from_hip(fa::launch_fwd_bf16(a, s));
     }
     return FA_ERR_DTYPE;
+}
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                   int Lq, int Lkv, int D, float scale, int causal, int window, fa_dtype_t dtype, void* stream) {
+    return fwd_impl(q, k, v, nullptr, 0, 0, o, lse, B, Hq, Hkv, Lq, Lkv, D, scale, causal, window, dtype, stream);
+}
+
+fa_status_t fa_fwd_masked(const void* q, const void* k, const void* v, const float* mask, long long mask_stride_b,
+                          long long mask_stride_h, void* o, float* lse, int B, int Hq, int Hkv, int Lq, int Lkv,
+                          int D, float scale, int causal, int window, fa_dtype_t dtype, void* stream) {
+    fa_status_t st = check_mask(mask, mask_stride_b, mask_stride_h);
+    if (st != FA_OK) return st;
+    return fwd_impl(q, k, v, mask, mask_stride_b, mask_stride_h, o, lse, B, Hq, Hkv, Lq, Lkv, D, scale, causal,
+                    window, dtype, stream);
 }
 
 fa_status_t fa_bwd_preprocess(const void* o, const void* dO, float* delta, int B, int Hq, int Lq, int D,
@@ -122,9 +153,10 @@ static fa_status_t bwd_common(const void* q, const void* k, const void* v, const
     return FA_OK;
 }
 
-fa_status_t fa_bwd_dkv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                       const float* delta, void* dk, void* dv, int B, int Hq, int Hkv, int Lq, int Lkv, int D,
-                       float scale, int causal, int window, fa_dtype_t dtype, void* stream) {
+static fa_status_t dkv_impl(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                            const float* delta, const float* mask, long long msb, long long msh, void* dk, void* dv,
+                            int B, int Hq, int Hkv, int Lq, int Lkv, int D, float scale, int causal, int window,
+                            fa_dtype_t dtype, void* stream) {
     if (!dk || !dv) return FA_ERR_NULL;
     fa_status_t st = bwd_common(q, k, v, dO, lse, delta, B, Hq, Hkv, Lq, Lkv, D, scale, window, dtype);
     if (st != FA_OK) return st;
@@ -132,7 +164,7 @@ fa_status_t fa_bwd_dkv(const void* q, const void* k, const void* v, const void* 
 
     fa::BwdArgs a{q, k, v, dO, lse, delta, nullptr, dk, dv, B, Hq, Hkv, Lq, Lkv, D,
                   (float)((double)scale * 1.4426950408889634), scale, causal ? 1 : 0,
-                  effective_window(window, Lq)};
+                  effective_window(window, Lq), mask, msb, msh, mask ? mask_vec4(mask, msb, msh, Lkv) : 0};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     switch (dtype) {
         case FA_F32: return from_hip(fa::launch_dkv_f32(a, s));
@@ -142,9 +174,27 @@ fa_status_t fa_bwd_dkv(const void* q, const void* k, const void* v, const void* 
     return FA_ERR_DTYPE;
 }
 
-fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                      const float* delta, void* dq, int B, int Hq, int Hkv, int Lq, int Lkv, int D, float scale,
-                      int causal, int window, fa_dtype_t dtype, void* stream) {
+fa_status_t fa_bwd_dkv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                       const float* delta, void* dk, void* dv, int B, int Hq, int Hkv, int Lq, int Lkv, int D,
+                       float scale, int causal, int window, fa_dtype_t dtype, void* stream) {
+    return dkv_impl(q, k, v, dO, lse, delta, nullptr, 0, 0, dk, dv, B, Hq, Hkv, Lq, Lkv, D, scale, causal, window,
+                    dtype, stream);
+}
+
+fa_status_t fa_bwd_dkv_masked(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                              const float* delta, const float* mask, long long mask_stride_b,
+                              long long mask_stride_h, void* dk, void* dv, int B, int Hq, int Hkv, int Lq, int Lkv,
+                              int D, float scale, int causal, int window, fa_dtype_t dtype, void* stream) {
+    fa_status_t st = check_mask(mask, mask_stride_b, mask_stride_h);
+    if (st != FA_OK) return st;
+    return dkv_impl(q, k, v, dO, lse, delta, mask, mask_stride_b, mask_stride_h, dk, dv, B, Hq, Hkv, Lq, Lkv, D,
+                    scale, causal, window, dtype, stream);
+}
+
+static fa_status_t dq_impl(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                           const float* delta, const float* mask, long long msb, long long msh, void* dq, int B,
+                           int Hq, int Hkv, int Lq, int Lkv, int D, float scale, int causal, int window,
+                           fa_dtype_t dtype, void* stream) {
     if (!dq) return FA_ERR_NULL;
     fa_status_t st = bwd_common(q, k, v, dO, lse, delta, B, Hq, Hkv, Lq, Lkv, D, scale, window, dtype);
     if (st != FA_OK) return st;
@@ -152,7 +202,7 @@ fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* d
 
     fa::BwdArgs a{q, k, v, dO, lse, delta, dq, nullptr, nullptr, B, Hq, Hkv, Lq, Lkv, D,
                   (float)((double)scale * 1.4426950408889634), scale, causal ? 1 : 0,
-                  effective_window(window, Lq)};
+                  effective_window(window, Lq), mask, msb, msh, mask ? mask_vec4(mask, msb, msh, Lkv) : 0};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     switch (dtype) {
         case FA_F32: return from_hip(fa::launch_dq_f32(a, s));
@@ -160,6 +210,23 @@ fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* d
         case FA_BF16: return from_hip(fa::launch_dq_bf16(a, s));
     }
     return FA_ERR_DTYPE;
+}
+
+fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                      const float* delta, void* dq, int B, int Hq, int Hkv, int Lq, int Lkv, int D, float scale,
+                      int causal, int window, fa_dtype_t dtype, void* stream) {
+    return dq_impl(q, k, v, dO, lse, delta, nullptr, 0, 0, dq, B, Hq, Hkv, Lq, Lkv, D, scale, causal, window, dtype,
+                   stream);
+}
+
+fa_status_t fa_bwd_dq_masked(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                             const float* delta, const float* mask, long long mask_stride_b, long long mask_stride_h,
+                             void* dq, int B, int Hq, int Hkv, int Lq, int Lkv, int D, float scale, int causal,
+                             int window, fa_dtype_t dtype, void* stream) {
+    fa_status_t st = check_mask(mask, mask_stride_b, mask_stride_h);
+    if (st != FA_OK) return st;
+    return dq_impl(q, k, v, dO, lse, delta, mask, mask_stride_b, mask_stride_h, dq, B, Hq, Hkv, Lq, Lkv, D, scale,
+                   causal, window, dtype, stream);
 }
 
 }  // extern "C"

@@ -301,6 +301,36 @@ __device__ __forceinline__ bool mask_ok(int i, int j, int causal, int window) {
     return !(causal && j > i) && !(window && i >= j && i - j >= window);
 }
 
+// ---------------------------------------------------------------------------
+// Additive mask of the masked entry points (ggmlR R/ag_flash_attn.R,
+// ag_flash_attention `mask`: 0 attends, -inf blocks; a finite value is added
+// to the scaled score). Values come back multiplied by log2(e), ready to be
+// added to c * S in the exp2 domain; positions past Lq or Lkv read as 0 (the
+// flags mask them anyway).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ const float* mask_slice(const float* m, long long msb, long long msh, int b, int h) {
+    return m + b * msb + h * msh;
+}
+__device__ __forceinline__ float mask_l2(const float* mb, int i, int j, int Lq, int Lkv) {
+    return (i < Lq && j < Lkv) ? mb[(size_t)i * Lkv + j] * kLog2e : 0.f;
+}
+// keys j0 .. j0+3 of row i; one 16-byte load when the caller guarantees the
+// alignment (vec) and the four keys exist
+__device__ __forceinline__ f32x4 mask4_l2(const float* mb, int i, int j0, int Lq, int Lkv, int vec) {
+    f32x4 r;
+    if (vec && i < Lq && j0 + 3 < Lkv) {
+        r = *reinterpret_cast<const f32x4*>(mb + (size_t)i * Lkv + j0);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = (i < Lq && j0 + e < Lkv) ? mb[(size_t)i * Lkv + j0 + e] : 0.f;
+    }
+    return r * kLog2e;
+}
+// LSE in the exp2 domain for the masked backward: a row with no allowed key
+// (lse = -inf) becomes +inf, so that c*S + mask - lse is -inf (p = 0) for
+// every entry of that row instead of NaN for entries the mask also blocks.
+__device__ __forceinline__ float lse_l2_masked(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
+
 // ===========================================================================
 // Forward
 // ===========================================================================
@@ -328,7 +358,7 @@ template <class T, int DMAX, int BKV, int RW, int DW> struct FwdCfg {
     static_assert(DS % 32 == 0 && BKV % 32 == 0, "tile shape");
 };
 
-template <class T, int DMAX, int BKV, int RW, int DW, int OCC>
+template <class T, int DMAX, int BKV, int RW, int DW, int OCC, bool MASK>
 __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_kernel(FwdArgs a) {
     using C = FwdCfg<T, DMAX, BKV, RW, DW>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -398,10 +428,23 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_kernel(FwdArgs a) {
             for (int gi = 0; gi < C::NKG; ++gi) Mma<T>::nat(s[kb], ld16(ka + gi * 32), qf[gi]);
         }
         if constexpr (DW > 1) reduce_partials<DW, C::NKB>(s, red, rw * DW, dw, lane);
+        if constexpr (MASK) {
+            // masked entry points: c S + log2(e) mask, from here on in the exp2 domain
+            const float* mb = mask_slice(a.mask, a.msb, a.msh, b, hq);
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd) {
+                    const f32x4 m4 = mask4_l2(mb, row, t0 + 32 * kb + 8 * qd + 4 * h, a.Lq, a.Lkv, a.mvec);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) s[kb][4 * qd + i] = fmaf(s[kb][4 * qd + i], c, m4[i]);
+                }
+        }
+        const float cs = MASK ? 1.f : c;  // factor that takes the scores below to the exp2 domain
 
         const bool need = (t0 + BKV > a.Lkv) || (a.causal && t0 + BKV - 1 > i0) ||
                           (a.window && i_last - t0 >= a.window);
-        // Row max of the raw scores (c >= 0 here, so it commutes with the scaling).
+        // Row max of the raw scores (cs >= 0 here, so it commutes with the scaling).
         float mx = -INFINITY;
         if (need) {
 #pragma unroll
@@ -419,7 +462,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_kernel(FwdArgs a) {
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_tile = mx == -INFINITY ? -INFINITY : mx * c;
+        const float m_tile = mx == -INFINITY ? -INFINITY : mx * cs;
         // The reference max moves only when a row's max grows by more than
         // 2^kRescaleLog2: probabilities stay below 2^kRescaleLog2 and O is
         // rescaled rarely. O, l and the LSE all use the same reference, so
@@ -446,7 +489,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_kernel(FwdArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float sv = s[kb][r];
-                    s[kb][r] = sv == -INFINITY ? 0.f : fast_exp2(fmaf(sv, c, -moff));
+                    s[kb][r] = sv == -INFINITY ? 0.f : fast_exp2(fmaf(sv, cs, -moff));
                     ls += s[kb][r];
                 }
         } else {
@@ -454,7 +497,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_kernel(FwdArgs a) {
             for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    s[kb][r] = fast_exp2(fmaf(s[kb][r], c, -moff));
+                    s[kb][r] = fast_exp2(fmaf(s[kb][r], cs, -moff));
                     ls += s[kb][r];
                 }
         }
@@ -583,7 +626,7 @@ template <class T, int DMAX, int BKV, int RW, int DW> struct DqCfg {
     static_assert(LDS <= kLdsBudget, "dQ tile does not fit in LDS");
 };
 
-template <class T, int DMAX, int BKV, int RW, int DW, int OCC>
+template <class T, int DMAX, int BKV, int RW, int DW, int OCC, bool MASK>
 __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_kernel(BwdArgs a) {
     using C = DqCfg<T, DMAX, BKV, RW, DW>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -616,8 +659,9 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_kernel(BwdArgs a) {
         df[gi] = in ? ld16(dop + (size_t)row * a.D + c * C::E) : zero4();
     }
     const size_t lrow = (size_t)(b * a.Hq + hq) * a.Lq + row;
-    const float lse2 = row < a.Lq ? a.lse[lrow] * kLog2e : 0.f;
+    const float lse2 = row < a.Lq ? (MASK ? lse_l2_masked(a.lse[lrow]) : a.lse[lrow] * kLog2e) : 0.f;
     const float dl = row < a.Lq ? a.delta[lrow] : 0.f;
+    const float* mb = MASK ? mask_slice(a.mask, a.msb, a.msh, b, hq) : nullptr;
 
     f32x16 acc[C::NDB];
 #pragma unroll
@@ -656,11 +700,18 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_kernel(BwdArgs a) {
         }
         const bool need = (t0 + BKV > a.Lkv) || (a.causal && t0 + BKV - 1 > i0) ||
                           (a.window && i_last - t0 >= a.window);
+        f32x4 m4[C::NKB][4];
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd)
+                m4[kb][qd] = MASK ? mask4_l2(mb, row, t0 + 32 * kb + 8 * qd + 4 * h, a.Lq, a.Lkv, a.mvec)
+                                  : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float p = fast_exp2(s[kb][r] * a.c - lse2);
+                float p = fast_exp2(MASK ? fmaf(s[kb][r], a.c, m4[kb][r >> 2][r & 3] - lse2) : s[kb][r] * a.c - lse2);
                 if (need) {
                     const int j = t0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
                     if (!(j < a.Lkv && mask_ok(row, j, a.causal, a.window))) p = 0.f;
@@ -760,7 +811,7 @@ template <class T, int DMAX, int BQ, int KW, int DW> struct DkvCfg {
     static_assert(LDS <= kLdsBudget, "dK/dV tile does not fit in LDS");
 };
 
-template <class T, int DMAX, int BQ, int KW, int DW, int OCC>
+template <class T, int DMAX, int BQ, int KW, int DW, int OCC, bool MASK>
 __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_kernel(BwdArgs a) {
     using C = DkvCfg<T, DMAX, BQ, KW, DW>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -871,7 +922,14 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_kernel(BwdArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 4 * qd + i;
-                    float p = fast_exp2(s[rb][r] * a.c - l4[i]);
+                    float p;
+                    if constexpr (MASK) {
+                        const float* mb = mask_slice(a.mask, a.msb, a.msh, b, g * reps + it / nqt);
+                        const float l2 = l4[i] == -INFINITY ? INFINITY : l4[i];
+                        p = fast_exp2(fmaf(s[rb][r], a.c, mask_l2(mb, q0 + rl + i, key, a.Lq, a.Lkv) - l2));
+                    } else {
+                        p = fast_exp2(s[rb][r] * a.c - l4[i]);
+                    }
                     if (need) {
                         const int irow = q0 + rl + i;
                         if (!(irow < a.Lq && mask_ok(irow, key, a.causal, a.window))) p = 0.f;
@@ -952,7 +1010,7 @@ template <class K> inline hipError_t set_lds(K kernel, int bytes) {
 template <class T, int DMAX, int BKV, int RW, int DW, int OCC>
 hipError_t launch_fwd_cfg(const FwdArgs& a, hipStream_t s) {
     using C = FwdCfg<T, DMAX, BKV, RW, DW>;
-    auto kern = fa_fwd_kernel<T, DMAX, BKV, RW, DW, OCC>;
+    auto kern = a.mask ? fa_fwd_kernel<T, DMAX, BKV, RW, DW, OCC, true> : fa_fwd_kernel<T, DMAX, BKV, RW, DW, OCC, false>;
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
     const long long nqt = (a.Lq + C::BQ - 1) / C::BQ;
@@ -964,7 +1022,7 @@ hipError_t launch_fwd_cfg(const FwdArgs& a, hipStream_t s) {
 template <class T, int DMAX, int BKV, int RW, int DW, int OCC>
 hipError_t launch_dq_cfg(const BwdArgs& a, hipStream_t s) {
     using C = DqCfg<T, DMAX, BKV, RW, DW>;
-    auto kern = fa_dq_kernel<T, DMAX, BKV, RW, DW, OCC>;
+    auto kern = a.mask ? fa_dq_kernel<T, DMAX, BKV, RW, DW, OCC, true> : fa_dq_kernel<T, DMAX, BKV, RW, DW, OCC, false>;
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
     const long long nqt = (a.Lq + C::BQ - 1) / C::BQ;
@@ -976,7 +1034,7 @@ hipError_t launch_dq_cfg(const BwdArgs& a, hipStream_t s) {
 template <class T, int DMAX, int BQ, int KW, int DW, int OCC>
 hipError_t launch_dkv_cfg(const BwdArgs& a, hipStream_t s) {
     using C = DkvCfg<T, DMAX, BQ, KW, DW>;
-    auto kern = fa_dkv_kernel<T, DMAX, BQ, KW, DW, OCC>;
+    auto kern = a.mask ? fa_dkv_kernel<T, DMAX, BQ, KW, DW, OCC, true> : fa_dkv_kernel<T, DMAX, BQ, KW, DW, OCC, false>;
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
     const long long nkt = (a.Lkv + C::BKV - 1) / C::BKV;

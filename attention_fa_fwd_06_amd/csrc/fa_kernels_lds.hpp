@@ -191,7 +191,7 @@ template <class T, int DMAX, int BKV, int RW, int DW, int NS> struct Fwd2Cfg {
     static_assert(NS >= 2 && DMAX % 64 == 0 && DS % 32 == 0, "configuration");
 };
 
-template <class T, int DMAX, int BKV, int RW, int DW, int OCC, int NS>
+template <class T, int DMAX, int BKV, int RW, int DW, int OCC, int NS, bool MASK>
 __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a) {
     using C = Fwd2Cfg<T, DMAX, BKV, RW, DW, NS>;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -307,6 +307,19 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
         }
         prio_valu();
         if constexpr (DW > 1) reduce_partials<DW, C::NKB>(s, red, rw * DW, dw, lane);
+        if constexpr (MASK) {
+            // masked entry points: c S + log2(e) mask, from here on in the exp2 domain
+            const float* mb = mask_slice(a.mask, a.msb, a.msh, b, hq);
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd) {
+                    const f32x4 m4 = mask4_l2(mb, row, t0 + 32 * kb + 8 * qd + 4 * h, a.Lq, a.Lkv, a.mvec);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) s[kb][4 * qd + i] = fmaf(s[kb][4 * qd + i], c, m4[i]);
+                }
+        }
+        const float cs = MASK ? 1.f : c;  // factor that takes the scores below to the exp2 domain
 
         // V^T fragments of the first output block, in flight during the softmax
         u32x4 vcur[C::NPG];
@@ -335,7 +348,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_tile = mx == -INFINITY ? -INFINITY : mx * c;
+        const float m_tile = mx == -INFINITY ? -INFINITY : mx * cs;
         const bool upd = m_tile > m_ref + kRescaleLog2;
         if (OCC < 2 || __ballot(upd)) {
             const float m_new = upd ? m_tile : m_ref;
@@ -353,7 +366,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float sv = s[kb][r];
-                    s[kb][r] = sv == -INFINITY ? 0.f : fast_exp2(fmaf(sv, c, -moff));
+                    s[kb][r] = sv == -INFINITY ? 0.f : fast_exp2(fmaf(sv, cs, -moff));
                     ls += s[kb][r];
                 }
         } else {
@@ -361,7 +374,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
             for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    s[kb][r] = fast_exp2(fmaf(s[kb][r], c, -moff));
+                    s[kb][r] = fast_exp2(fmaf(s[kb][r], cs, -moff));
                     ls += s[kb][r];
                 }
         }
@@ -425,7 +438,7 @@ template <class T, int DMAX, int BKV, int RW, int DW, int NS> struct Dq2Cfg {
     static_assert(NS >= 2 && DMAX % 64 == 0 && DS % 32 == 0, "configuration");
 };
 
-template <class T, int DMAX, int BKV, int RW, int DW, int OCC, int NS>
+template <class T, int DMAX, int BKV, int RW, int DW, int OCC, int NS, bool MASK>
 __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a) {
     using C = Dq2Cfg<T, DMAX, BKV, RW, DW, NS>;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -465,7 +478,8 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
         df[gi] = buf_ld16(rdo, off);
     }
     const size_t lrow = (size_t)(b * a.Hq + hq) * a.Lq + row;
-    const float lse2 = row < a.Lq ? a.lse[lrow] * kLog2e : 0.f;
+    const float lse2 = row < a.Lq ? (MASK ? lse_l2_masked(a.lse[lrow]) : a.lse[lrow] * kLog2e) : 0.f;
+    const float* mb = MASK ? mask_slice(a.mask, a.msb, a.msh, b, hq) : nullptr;
     const float dl = row < a.Lq ? a.delta[lrow] : 0.f;
 
     f32x16 acc[C::NDB];
@@ -557,12 +571,23 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
 
         const bool need = (t0 + BKV > a.Lkv) || (a.causal && t0 + BKV - 1 > i0) ||
                           (a.window && i_last - t0 >= a.window);
+        f32x4 m4[C::NKB][4];
+        if constexpr (MASK) {
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd) {
+                    m4[kb][qd] = mask4_l2(mb, row, t0 + 32 * kb + 8 * qd + 4 * h, a.Lq, a.Lkv, a.mvec);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) m4[kb][qd][i] -= lse2;
+                }
+        }
         auto dscore = [&](auto masked) {
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float p = fast_exp2(fmaf(s[kb][r], a.c, -lse2));
+                    float p = fast_exp2(fmaf(s[kb][r], a.c, MASK ? m4[kb][r >> 2][r & 3] : -lse2));
                     if constexpr (decltype(masked)::value) {
                         const int j = t0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3), dd = row - j;
                         p = ((j < a.Lkv) & (dd >= dlo) & (dd < dhi)) ? p : 0.f;
@@ -638,7 +663,7 @@ template <class T, int DMAX, int BQ, int KW, int DW, int NS> struct Dkv2Cfg {
     static_assert(NS >= 2 && DMAX % 64 == 0 && DS % 32 == 0 && BQ >= 32 && BQ <= 64, "configuration");
 };
 
-template <class T, int DMAX, int BQ, int KW, int DW, int OCC, int NS>
+template <class T, int DMAX, int BQ, int KW, int DW, int OCC, int NS, bool MASK>
 __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_lds_kernel(BwdArgs a) {
     using C = Dkv2Cfg<T, DMAX, BQ, KW, DW, NS>;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -788,7 +813,14 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_lds_kernel(BwdArgs a
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 4 * qd + i;
-                    float p = fast_exp2(fmaf(s[rb][r], a.c, -l4[i] * kLog2e));
+                    float p;
+                    if constexpr (MASK) {
+                        const float* mb = mask_slice(a.mask, a.msb, a.msh, b, g * reps + it / nqt);
+                        p = fast_exp2(fmaf(s[rb][r], a.c, mask_l2(mb, q0 + rl + i, key, a.Lq, a.Lkv) -
+                                                              lse_l2_masked(l4[i])));
+                    } else {
+                        p = fast_exp2(fmaf(s[rb][r], a.c, -l4[i] * kLog2e));
+                    }
                     if (need) {
                         const int irow = q0 + rl + i;
                         if (!(irow < a.Lq && mask_ok(irow, key, a.causal, a.window))) p = 0.f;
@@ -879,7 +911,7 @@ template <class T, int DMAX, int BQ, int KW, int DW> struct DkvPipeCfg {
     static_assert(DS % 64 == 0 && (BQ == 32 || BQ == 64) && (DW == 1 || DW == 2), "configuration");
 };
 
-template <class T, int DMAX, int BQ, int KW, int DW, int OCC, int PRIO>
+template <class T, int DMAX, int BQ, int KW, int DW, int OCC, int PRIO, bool MASK>
 __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, int pair) {
     using C = DkvPipeCfg<T, DMAX, BQ, KW, DW>;
     using T8 = typename Vec8<T>::type;
@@ -1067,12 +1099,26 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
                 if constexpr (V) {
                     // P = exp2(c S - log2(e) lse), masked entries 0; x[rb][4 qd + i] is
                     // row 32 rb + 8 qd + 4 h + i of the tile
+                    if constexpr (MASK) {
+                        // log2(e) (mask - lse) of each element; rows without any allowed key
+                        // get -inf
+                        const float* mb = mask_slice(a.mask, a.msb, a.msh, b, g * reps + hq_cnt);
+#pragma unroll
+                        for (int rb = 0; rb < C::NRB; ++rb)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int irow = q0 + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
+                                rv[rb][r >> 2][r & 3] =
+                                    mask_l2(mb, irow, key, a.Lq, a.Lkv) - lse_l2_masked(rv[rb][r >> 2][r & 3]);
+                            }
+                    }
                     auto probs = [&](auto masked) {
 #pragma unroll
                         for (int rb = 0; rb < C::NRB; ++rb)
 #pragma unroll
                             for (int r = 0; r < 16; ++r) {
-                                float p = fast_exp2(fmaf(x[rb][r], a.c, -rv[rb][r >> 2][r & 3] * kLog2e));
+                                float p = fast_exp2(fmaf(x[rb][r], a.c, MASK ? rv[rb][r >> 2][r & 3]
+                                                                              : -rv[rb][r >> 2][r & 3] * kLog2e));
                                 if constexpr (decltype(masked)::value) {
                                     const int irow = q0 + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3), dd = irow - key;
                                     p = ((irow < a.Lq) & (dd >= dlo) & (dd < dhi)) ? p : 0.f;
@@ -1174,7 +1220,8 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
 template <class T, int DMAX, int BKV, int RW, int DW, int OCC, int NS>
 hipError_t launch_fwd2(const FwdArgs& a, hipStream_t s) {
     using C = Fwd2Cfg<T, DMAX, BKV, RW, DW, NS>;
-    auto kern = fa_fwd_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS>;
+    auto kern = a.mask ? fa_fwd_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS, true>
+                       : fa_fwd_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS, false>;
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
     const long long grid = (long long)((a.Lq + C::BQ - 1) / C::BQ) * a.B * a.Hq;
@@ -1184,7 +1231,8 @@ hipError_t launch_fwd2(const FwdArgs& a, hipStream_t s) {
 template <class T, int DMAX, int BKV, int RW, int DW, int OCC, int NS>
 hipError_t launch_dq2(const BwdArgs& a, hipStream_t s) {
     using C = Dq2Cfg<T, DMAX, BKV, RW, DW, NS>;
-    auto kern = fa_dq_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS>;
+    auto kern = a.mask ? fa_dq_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS, true>
+                       : fa_dq_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS, false>;
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
     const long long grid = (long long)((a.Lq + C::BQ - 1) / C::BQ) * a.B * a.Hq;
@@ -1194,7 +1242,8 @@ hipError_t launch_dq2(const BwdArgs& a, hipStream_t s) {
 template <class T, int DMAX, int BQ, int KW, int DW, int OCC, int NS>
 hipError_t launch_dkv2(const BwdArgs& a, hipStream_t s) {
     using C = Dkv2Cfg<T, DMAX, BQ, KW, DW, NS>;
-    auto kern = fa_dkv_lds_kernel<T, DMAX, BQ, KW, DW, OCC, NS>;
+    auto kern = a.mask ? fa_dkv_lds_kernel<T, DMAX, BQ, KW, DW, OCC, NS, true>
+                       : fa_dkv_lds_kernel<T, DMAX, BQ, KW, DW, OCC, NS, false>;
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
     const long long grid = (long long)((a.Lkv + C::BKV - 1) / C::BKV) * a.B * a.Hkv;
@@ -1209,7 +1258,8 @@ constexpr int kPairMinGrid = 256;
 template <class T, int DMAX, int BQ, int KW, int DW, int OCC, int PRIO>
 hipError_t launch_dkv_pipe(const BwdArgs& a, hipStream_t s) {
     using C = DkvPipeCfg<T, DMAX, BQ, KW, DW>;
-    auto kern = fa_dkv_pipe_kernel<T, DMAX, BQ, KW, DW, OCC, PRIO>;
+    auto kern = a.mask ? fa_dkv_pipe_kernel<T, DMAX, BQ, KW, DW, OCC, PRIO, true>
+                       : fa_dkv_pipe_kernel<T, DMAX, BQ, KW, DW, OCC, PRIO, false>;
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
     const long long nkt = (a.Lkv + C::BKV - 1) / C::BKV;

@@ -17,6 +17,11 @@ struct FwdArgs {
     float c;      // scale * log2(e): scores are handled in the exp2 domain
     int causal;
     int window;
+    // additive mask (masked entry points only; nullptr otherwise): element
+    // (b, h, i, j) at mask[b * msb + h * msh + i * Lkv + j]
+    const float* mask;
+    long long msb, msh;
+    int mvec;     // rows of four keys may be read as one 16-byte load
 };
 
 // Backward pre-pass: delta = rowsum(dO * O) over rows of length D.
@@ -44,6 +49,9 @@ struct BwdArgs {
     float scale;  // applied once to dQ and dK in the epilogue
     int causal;
     int window;
+    const float* mask;  // as in FwdArgs
+    long long msb, msh;
+    int mvec;
 };
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);

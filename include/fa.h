@@ -6,6 +6,8 @@
  *   fa_bwd_preprocess Delta = rowsum(dO * O)
  *   fa_bwd_dkv        dK, dV (each workgroup owns a block of K/V rows; no atomics)
  *   fa_bwd_dq         dQ
+ * and masked variants of the forward and both backward calls that take an
+ * additive mask tensor (fa_fwd_masked, fa_bwd_dkv_masked, fa_bwd_dq_masked).
  *
  * Sources: mlx-bun flash-attention.ts (flashForward and flashBackward host
  * functions and the forward, D pre-pass, dK/dV and dQ shaders); the MLX pull
@@ -75,7 +77,7 @@ typedef enum {
     FA_ERR_HEADDIM = -3, /* D outside [32, 512] ([32, 256] for FA_F32) or not a multiple of 8 */
     FA_ERR_DTYPE = -4,   /* dtype is not one of fa_dtype_t */
     FA_ERR_ALIGN = -5,   /* a pointer is not 16-byte aligned */
-    FA_ERR_ARG = -6,     /* negative window or non-finite scale */
+    FA_ERR_ARG = -6,     /* negative window, non-finite scale, or a mask stride outside [0, 2^40] */
     FA_ERR_LAUNCH = -7   /* the HIP kernel launch failed */
 } fa_status_t;
 
@@ -119,6 +121,49 @@ fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* d
                       const float* lse, const float* delta, void* dq,
                       int B, int Hq, int Hkv, int Lq, int Lkv, int D,
                       float scale, int causal, int window, fa_dtype_t dtype, void* stream);
+
+/*
+ * Masked variants (ggmlR R/ag_flash_attn.R, ag_flash_attention: an optional
+ * numeric mask per (query, key), 0 to attend and -Inf to block, used for the
+ * forward and for the gradient alike).
+ *
+ * mask is a DEVICE pointer to float32 values; the value for batch b, query
+ * head h, query row i and key j is
+ *     mask[b * mask_stride_b + h * mask_stride_h + i * Lkv + j]
+ * with the strides in elements and 0 broadcasting over that dimension: one
+ * [Lq, Lkv] mask for every head has both strides 0, a [B, 1, Lq, Lkv] mask
+ * has mask_stride_b = Lq*Lkv and mask_stride_h = 0, a [B, Hq, Lq, Lkv] mask
+ * Hq*Lq*Lkv and Lq*Lkv. Rows are query-major (i is the slow index), the
+ * memory order of ggml's [n_kv, n_q] mask.
+ * The value is added to the scaled score before the softmax:
+ *     s_ij = scale * q_i . k_j + mask_ij,
+ * so 0 leaves a score alone and -inf removes the pair; the causal flag and
+ * the window apply on top, and lse is the natural-log logsumexp of these
+ * s_ij. Values must be finite or -inf (NaN and +inf are not checked and give
+ * undefined results). The three calls of one step must get the same mask;
+ * fa_bwd_preprocess needs none. A row whose keys are all removed gets O = 0,
+ * lse = -inf and no gradient. The mask carries no gradient.
+ * Extra checks: mask non-NULL (FA_ERR_NULL) and 4-byte aligned (FA_ERR_ALIGN);
+ * both strides in [0, 2^40] (FA_ERR_ARG). The mask is read with 16-byte loads
+ * when it is 16-byte aligned and Lkv and both strides are multiples of 4, with
+ * 4-byte loads otherwise. Everything else is as for the unmasked calls.
+ */
+fa_status_t fa_fwd_masked(const void* q, const void* k, const void* v, const float* mask,
+                          long long mask_stride_b, long long mask_stride_h, void* o, float* lse,
+                          int B, int Hq, int Hkv, int Lq, int Lkv, int D,
+                          float scale, int causal, int window, fa_dtype_t dtype, void* stream);
+
+fa_status_t fa_bwd_dkv_masked(const void* q, const void* k, const void* v, const void* dO,
+                              const float* lse, const float* delta, const float* mask,
+                              long long mask_stride_b, long long mask_stride_h, void* dk, void* dv,
+                              int B, int Hq, int Hkv, int Lq, int Lkv, int D,
+                              float scale, int causal, int window, fa_dtype_t dtype, void* stream);
+
+fa_status_t fa_bwd_dq_masked(const void* q, const void* k, const void* v, const void* dO,
+                             const float* lse, const float* delta, const float* mask,
+                             long long mask_stride_b, long long mask_stride_h, void* dq,
+                             int B, int Hq, int Hkv, int Lq, int Lkv, int D,
+                             float scale, int causal, int window, fa_dtype_t dtype, void* stream);
 
 /* Static, never-NULL description of a status code. */
 const char* fa_status_string(fa_status_t s);

@@ -35,7 +35,7 @@ def lib():
     return fa.load_library()
 
 
-def test_header_declares_the_four_calls():
+def test_header_declares_every_exported_call():
     assert _declared() == sorted(fa.EXPORTS)
 
 
@@ -169,3 +169,60 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(fa, "_lib", None)
     with pytest.raises(RuntimeError):
         fa.load_library(str(tmp_path / "nope.so"))
+
+
+def _fwdm(lib, mask=P, msb=0, msh=0, **kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=4, Hkv=2, Lq=64, Lkv=64, D=64, scale=0.125, causal=1, window=0,
+                dtype=fa.FA_BF16)
+    args.update(kw)
+    a = args
+    return lib.fa_fwd_masked(a["q"], a["k"], a["v"], mask, msb, msh, a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                             a["Lq"], a["Lkv"], a["D"], a["scale"], a["causal"], a["window"], a["dtype"], None)
+
+
+def _dkvm(lib, mask=P, msb=0, msh=0, D=64, dtype=fa.FA_BF16):
+    return lib.fa_bwd_dkv_masked(P, P, P, P, P, P, mask, msb, msh, P, P, 1, 4, 2, 64, 64, D, 0.125, 1, 0, dtype, None)
+
+
+def _dqm(lib, mask=P, msb=0, msh=0, D=64, dtype=fa.FA_BF16):
+    return lib.fa_bwd_dq_masked(P, P, P, P, P, P, mask, msb, msh, P, 1, 4, 2, 64, 64, D, 0.125, 1, 0, dtype, None)
+
+
+@pytest.mark.parametrize("mask,msb,msh,code", [
+    (None, 0, 0, NULL),
+    (P + 2, 0, 0, ALIGN),
+    (P + 4, 0, 0, OK),  # 4-byte aligned is enough (4-byte loads); launch is not reached below
+    (P, -1, 0, ARG),
+    (P, 0, -4096, ARG),
+    (P, (1 << 40) + 4, 0, ARG),
+])
+def test_masked_calls_check_the_mask(lib, mask, msb, msh, code):
+    if code == OK:
+        # a valid mask with an invalid head dim: the call must fail on the head dim, never launch
+        assert _fwdm(lib, mask, msb, msh, D=36) == HEADDIM
+        assert _dkvm(lib, mask, msb, msh, D=36) == HEADDIM
+        assert _dqm(lib, mask, msb, msh, D=36) == HEADDIM
+        return
+    assert _fwdm(lib, mask, msb, msh) == code
+    assert _dkvm(lib, mask, msb, msh) == code
+    assert _dqm(lib, mask, msb, msh) == code
+
+
+def test_masked_calls_check_everything_else(lib):
+    assert _fwdm(lib, q=None) == NULL
+    assert _fwdm(lib, o=P + 8) == ALIGN
+    assert _fwdm(lib, dtype=5) == DTYPE
+    assert _fwdm(lib, window=-1) == ARG
+    assert _fwdm(lib, Hq=3, Hkv=2) == SHAPE
+    assert _dkvm(lib, dtype=9) == DTYPE
+    assert _dqm(lib, D=520) == HEADDIM
+    assert lib.fa_bwd_dkv_masked(P, P, P, P, P, P, P, 0, 0, None, P, 1, 4, 2, 64, 64, 64, 0.1, 1, 0,
+                                 fa.FA_F16, None) == NULL
+    assert lib.fa_bwd_dq_masked(P, P, P, P, P, P, P, 0, 0, P + 4, 1, 4, 2, 64, 64, 64, 0.1, 1, 0,
+                                fa.FA_F16, None) == ALIGN
+
+
+def test_binding_mask_shape_checks(lib):
+    m = torch.zeros(64, 64)
+    with pytest.raises(ValueError):
+        fa._mask_args(m, 1, 4, 64, 64, torch.device("cuda", 0))  # not on the GPU
