@@ -86,6 +86,18 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
     return (n & 7) ? i : (i & 7) * (n >> 3) + (i >> 3);
 }
 
+// Calls f(t + S, integral_constant<S>) for S = S0 .. NS-1 while t + S < n: a
+// loop over a ring of NS stages unrolled by NS, so that every stage offset is
+// a compile-time constant (LDS addresses become immediate offsets).
+template <int S, int NS, class F> __device__ __forceinline__ void unroll_slots(int t, int n, F& f) {
+    if constexpr (S < NS) {
+        if (t + S < n) {
+            f(t + S, std::integral_constant<int, S>{});
+            unroll_slots<S + 1, NS>(t, n, f);
+        }
+    }
+}
+
 // Scheduling fence: keeps a chain's LDS reads ahead of its MFMAs, so that all
 // of them are in flight together and each MFMA waits only for its own
 // fragment (left alone, the scheduler serialises read -> wait -> MFMA).
@@ -257,154 +269,154 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
     const int dlo = a.causal ? 0 : INT_MIN;
     const int dhi = a.window ? a.window : INT_MAX;
 
-    auto issue = [&](int t) {
-        char* st = smem + (t % NS) * C::STAGEB;
+    auto issue = [&](int t, auto slot) {
+        char* st = smem + decltype(slot)::value * C::STAGEB;
         dma.issue(rk, st, (t_lo + t) * BKV, D, w);
         dma.issue(rv, st + C::TILEB, (t_lo + t) * BKV, D, w);
     };
     constexpr int LPT = 2 * DmaPlan<BKV, DMAX, C::NW>::NIW;  // DMA instructions per tile per wave
 
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-        if (s < n_t) issue(s);
+    unroll_slots<0, NS - 1>(0, n_t, issue);
 
-    for (int t = 0; t < n_t; ++t) {
-        if (t + NS - 2 < n_t) wait_vm<(NS - 2) * LPT>();
-        else wait_vm<0>();
-        lds_barrier();  // tile t visible to all waves; every wave is done with tile t-1
-        if (t + NS - 1 < n_t) issue(t + NS - 1);
+    auto step = [&](int t, auto slot) {
+        constexpr int SL = decltype(slot)::value;  // stage of tile t
+            if (t + NS - 2 < n_t) wait_vm<(NS - 2) * LPT>();
+            else wait_vm<0>();
+            lds_barrier();  // tile t visible to all waves; every wave is done with tile t-1
+            if (t + NS - 1 < n_t) issue(t + NS - 1, std::integral_constant<int, (SL + NS - 1) % NS>{});
 
-        const char* kl = smem + (t % NS) * C::STAGEB;
-        const char* vl = kl + C::TILEB;
-        const int t0 = (t_lo + t) * BKV;
-        // S^T = K Q^T in batches of FB fragments; each batch's K fragments are
-        // requested before the previous batch's MFMAs
-        f32x16 s[C::NKB];
-        {
-            constexpr int FB = C::NKG < 8 ? C::NKG : 8, BPK = C::NKG / FB, NB = C::NKB * BPK;
-            auto load = [&](int k, u32x4 (&f)[FB]) {
-#pragma unroll
-                for (int i = 0; i < FB; ++i) f[i] = ld16(kl + to.natural(32 * (k / BPK), (k % BPK) * FB + i, cb));
-            };
-            u32x4 cur[FB];
-            load(0, cur);
+            const char* kl = smem + SL * C::STAGEB;
+            const char* vl = kl + C::TILEB;
+            const int t0 = (t_lo + t) * BKV;
+            // S^T = K Q^T in batches of FB fragments; each batch's K fragments are
+            // requested before the previous batch's MFMAs
+            f32x16 s[C::NKB];
+            {
+                constexpr int FB = C::NKG < 8 ? C::NKG : 8, BPK = C::NKG / FB, NB = C::NKB * BPK;
+                auto load = [&](int k, u32x4 (&f)[FB]) {
+    #pragma unroll
+                    for (int i = 0; i < FB; ++i) f[i] = ld16(kl + to.natural(32 * (k / BPK), (k % BPK) * FB + i, cb));
+                };
+                u32x4 cur[FB];
+                load(0, cur);
+                prio_mfma();
+    #pragma unroll
+                for (int k = 0; k < NB; ++k) {
+                    u32x4 nxt[FB];
+                    if (k + 1 < NB) load(k + 1, nxt);
+                    sched_fence();
+                    const int kb = k / BPK, g0 = (k % BPK) * FB;
+                    if (g0 == 0) s[kb] = zero16();
+    #pragma unroll
+                    for (int i = 0; i < FB; ++i) Mma<T>::nat(s[kb], cur[i], qf[g0 + i]);
+                    sched_fence();
+                    if (k + 1 < NB) {
+    #pragma unroll
+                        for (int i = 0; i < FB; ++i) cur[i] = nxt[i];
+                    }
+                }
+            }
+            prio_valu();
+            if constexpr (DW > 1) reduce_partials<DW, C::NKB>(s, red, rw * DW, dw, lane);
+            if constexpr (MASK) {
+                // masked entry points: c S + log2(e) mask, from here on in the exp2 domain
+                const float* mb = mask_slice(a.mask, a.msb, a.msh, b, hq);
+    #pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+    #pragma unroll
+                    for (int qd = 0; qd < 4; ++qd) {
+                        const f32x4 m4 = mask4_l2(mb, row, t0 + 32 * kb + 8 * qd + 4 * h, a.Lq, a.Lkv, a.mvec);
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i) s[kb][4 * qd + i] = fmaf(s[kb][4 * qd + i], c, m4[i]);
+                    }
+            }
+            const float cs = MASK ? 1.f : c;  // factor that takes the scores below to the exp2 domain
+
+            // V^T fragments of the first output block, in flight during the softmax
+            u32x4 vcur[C::NPG];
+    #pragma unroll
+            for (int gg = 0; gg < C::NPG; ++gg)
+                vcur[gg] = rd_tr(vl + to.transposed(gg, 0, cb, 0), vl + to.transposed(gg, 0, cb, 1));
+
+            const bool need = (t0 + BKV > a.Lkv) || (a.causal && t0 + BKV - 1 > i0) ||
+                              (a.window && i_last - t0 >= a.window);
+            float mx = -INFINITY;
+            if (need) {
+                // key j allowed for this row: j < Lkv and row - j in [dlo, dhi)
+    #pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int j = t0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3), dd = row - j;
+                        const bool ok = (j < a.Lkv) & (dd >= dlo) & (dd < dhi);
+                        s[kb][r] = ok ? s[kb][r] : -INFINITY;
+                        mx = fmaxf(mx, s[kb][r]);
+                    }
+            } else {
+    #pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_tile = mx == -INFINITY ? -INFINITY : mx * cs;
+            const bool upd = m_tile > m_ref + kRescaleLog2;
+            if (OCC < 2 || __ballot(upd)) {
+                const float m_new = upd ? m_tile : m_ref;
+                const float alpha = upd ? fast_exp2(m_ref - m_new) : 1.f;
+                l_run *= alpha;
+    #pragma unroll
+                for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
+                m_ref = m_new;
+            }
+            const float moff = m_ref == -INFINITY ? 0.f : m_ref;
+            float ls = 0.f;
+            if (need) {
+    #pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float sv = s[kb][r];
+                        s[kb][r] = sv == -INFINITY ? 0.f : fast_exp2(fmaf(sv, cs, -moff));
+                        ls += s[kb][r];
+                    }
+            } else {
+    #pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        s[kb][r] = fast_exp2(fmaf(s[kb][r], cs, -moff));
+                        ls += s[kb][r];
+                    }
+            }
+            l_run += ls;
+
+            // O^T += V^T P^T, one 32-wide output block at a time; the next block's
+            // fragments are requested before this block's MFMAs
+            PF<T> pf[C::NPG];
+    #pragma unroll
+            for (int gg = 0; gg < C::NPG; ++gg) pf[gg] = make_pf<T>(s[gg >> 1], gg & 1);
             prio_mfma();
-#pragma unroll
-            for (int k = 0; k < NB; ++k) {
-                u32x4 nxt[FB];
-                if (k + 1 < NB) load(k + 1, nxt);
+    #pragma unroll
+            for (int db = 0; db < C::NDB; ++db) {
+                u32x4 vnxt[C::NPG];
+                if (db + 1 < C::NDB) {
+    #pragma unroll
+                    for (int gg = 0; gg < C::NPG; ++gg)
+                        vnxt[gg] = rd_tr(vl + to.transposed(gg, db + 1, cb, 0), vl + to.transposed(gg, db + 1, cb, 1));
+                }
                 sched_fence();
-                const int kb = k / BPK, g0 = (k % BPK) * FB;
-                if (g0 == 0) s[kb] = zero16();
-#pragma unroll
-                for (int i = 0; i < FB; ++i) Mma<T>::nat(s[kb], cur[i], qf[g0 + i]);
+    #pragma unroll
+                for (int gg = 0; gg < C::NPG; ++gg) Mma<T>::nat(o[db], vcur[gg], pf[gg].v);
                 sched_fence();
-                if (k + 1 < NB) {
-#pragma unroll
-                    for (int i = 0; i < FB; ++i) cur[i] = nxt[i];
+                if (db + 1 < C::NDB) {
+    #pragma unroll
+                    for (int gg = 0; gg < C::NPG; ++gg) vcur[gg] = vnxt[gg];
                 }
             }
-        }
-        prio_valu();
-        if constexpr (DW > 1) reduce_partials<DW, C::NKB>(s, red, rw * DW, dw, lane);
-        if constexpr (MASK) {
-            // masked entry points: c S + log2(e) mask, from here on in the exp2 domain
-            const float* mb = mask_slice(a.mask, a.msb, a.msh, b, hq);
-#pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-                for (int qd = 0; qd < 4; ++qd) {
-                    const f32x4 m4 = mask4_l2(mb, row, t0 + 32 * kb + 8 * qd + 4 * h, a.Lq, a.Lkv, a.mvec);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) s[kb][4 * qd + i] = fmaf(s[kb][4 * qd + i], c, m4[i]);
-                }
-        }
-        const float cs = MASK ? 1.f : c;  // factor that takes the scores below to the exp2 domain
-
-        // V^T fragments of the first output block, in flight during the softmax
-        u32x4 vcur[C::NPG];
-#pragma unroll
-        for (int gg = 0; gg < C::NPG; ++gg)
-            vcur[gg] = rd_tr(vl + to.transposed(gg, 0, cb, 0), vl + to.transposed(gg, 0, cb, 1));
-
-        const bool need = (t0 + BKV > a.Lkv) || (a.causal && t0 + BKV - 1 > i0) ||
-                          (a.window && i_last - t0 >= a.window);
-        float mx = -INFINITY;
-        if (need) {
-            // key j allowed for this row: j < Lkv and row - j in [dlo, dhi)
-#pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int j = t0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3), dd = row - j;
-                    const bool ok = (j < a.Lkv) & (dd >= dlo) & (dd < dhi);
-                    s[kb][r] = ok ? s[kb][r] : -INFINITY;
-                    mx = fmaxf(mx, s[kb][r]);
-                }
-        } else {
-#pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_tile = mx == -INFINITY ? -INFINITY : mx * cs;
-        const bool upd = m_tile > m_ref + kRescaleLog2;
-        if (OCC < 2 || __ballot(upd)) {
-            const float m_new = upd ? m_tile : m_ref;
-            const float alpha = upd ? fast_exp2(m_ref - m_new) : 1.f;
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
-            m_ref = m_new;
-        }
-        const float moff = m_ref == -INFINITY ? 0.f : m_ref;
-        float ls = 0.f;
-        if (need) {
-#pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float sv = s[kb][r];
-                    s[kb][r] = sv == -INFINITY ? 0.f : fast_exp2(fmaf(sv, cs, -moff));
-                    ls += s[kb][r];
-                }
-        } else {
-#pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    s[kb][r] = fast_exp2(fmaf(s[kb][r], cs, -moff));
-                    ls += s[kb][r];
-                }
-        }
-        l_run += ls;
-
-        // O^T += V^T P^T, one 32-wide output block at a time; the next block's
-        // fragments are requested before this block's MFMAs
-        PF<T> pf[C::NPG];
-#pragma unroll
-        for (int gg = 0; gg < C::NPG; ++gg) pf[gg] = make_pf<T>(s[gg >> 1], gg & 1);
-        prio_mfma();
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-            u32x4 vnxt[C::NPG];
-            if (db + 1 < C::NDB) {
-#pragma unroll
-                for (int gg = 0; gg < C::NPG; ++gg)
-                    vnxt[gg] = rd_tr(vl + to.transposed(gg, db + 1, cb, 0), vl + to.transposed(gg, db + 1, cb, 1));
-            }
-            sched_fence();
-#pragma unroll
-            for (int gg = 0; gg < C::NPG; ++gg) Mma<T>::nat(o[db], vcur[gg], pf[gg].v);
-            sched_fence();
-            if (db + 1 < C::NDB) {
-#pragma unroll
-                for (int gg = 0; gg < C::NPG; ++gg) vcur[gg] = vnxt[gg];
-            }
-        }
-        prio_valu();
-    }
+            prio_valu();
+    };
+    for (int t = 0; t < n_t; t += NS) unroll_slots<0, NS>(t, n_t, step);
 
     const float l = l_run + __shfl_xor(l_run, 32);
     if (row < a.Lq) {
