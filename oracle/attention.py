@@ -139,7 +139,7 @@ def _bias(bias, B, Hq, Lq, Lkv):
 
 
 def forward(q, k, v, scale, causal=False, window=0, bias=None):
-    """O [B,Hq,Lq,D] and natural-log LSE [B,Hq,Lq] for float64 inputs.
+    """O [B,Hq,Lq,Dv] and natural-log LSE [B,Hq,Lq] for float64 inputs (v: [B,Hkv,Lkv,Dv]).
 
     bias: optional additive mask broadcastable to [B, Hq, Lq, Lkv]."""
     B, Hq, Lq, D = q.shape
