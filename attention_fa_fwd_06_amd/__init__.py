@@ -11,8 +11,9 @@ caller-allocated tensors):
     fa_bwd_preprocess(o, do, delta)
     fa_bwd_dkv(q, k, v, do, lse, delta, dk, dv, scale, causal, window)
     fa_bwd_dq(q, k, v, do, lse, delta, dq, scale, causal, window)
-    fa_fwd_masked, fa_bwd_dkv_masked, fa_bwd_dq_masked: the same with an
-    additive float32 mask tensor after v (resp. delta)
+    fa_fwd_masked, fa_bwd_dkv_masked, fa_bwd_dq_masked, fa_fwd_ex, fa_bwd_dkv_ex,
+    fa_bwd_dq_ex: reached through the calls above when a mask is given or v's
+    head dim Dv differs from q's D (then o, dO and dv are [.., Dv])
 Convenience wrappers that allocate their outputs:
     forward(q, k, v, scale=None, causal=False, window=0, mask=None) -> (o, lse)
     backward(q, k, v, o, lse, do, scale=None, causal=False, window=0, mask=None) -> (dq, dk, dv)
@@ -43,7 +44,7 @@ STATUS = {
     -7: "FA_ERR_LAUNCH",
 }
 EXPORTS = ("fa_fwd", "fa_bwd_preprocess", "fa_bwd_dkv", "fa_bwd_dq", "fa_fwd_masked", "fa_bwd_dkv_masked",
-           "fa_bwd_dq_masked", "fa_status_string")
+           "fa_bwd_dq_masked", "fa_fwd_ex", "fa_bwd_dkv_ex", "fa_bwd_dq_ex", "fa_status_string")
 
 _lib = None
 
@@ -73,8 +74,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_masked.argtypes = [P, P, P, P, LL, LL, P, P, I, I, I, I, I, I, F, I, I, I, P]
     lib.fa_bwd_dkv_masked.argtypes = [P, P, P, P, P, P, P, LL, LL, P, P, I, I, I, I, I, I, F, I, I, I, P]
     lib.fa_bwd_dq_masked.argtypes = [P, P, P, P, P, P, P, LL, LL, P, I, I, I, I, I, I, F, I, I, I, P]
+    lib.fa_fwd_ex.argtypes = [P, P, P, P, P, P, I, P]
+    lib.fa_bwd_dkv_ex.argtypes = [P, P, P, P, P, P, P, P, P, I, P]
+    lib.fa_bwd_dq_ex.argtypes = [P, P, P, P, P, P, P, P, I, P]
     for fn in ("fa_fwd", "fa_bwd_preprocess", "fa_bwd_dkv", "fa_bwd_dq", "fa_fwd_masked", "fa_bwd_dkv_masked",
-               "fa_bwd_dq_masked"):
+               "fa_bwd_dq_masked", "fa_fwd_ex", "fa_bwd_dkv_ex", "fa_bwd_dq_ex"):
         getattr(lib, fn).restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -131,13 +135,15 @@ def _shape4(t, name):
 
 
 def _attn_shapes(q, k, v):
+    """(B, Hq, Hkv, Lq, Lkv, D, Dv) of q [B,Hq,Lq,D], k [B,Hkv,Lkv,D], v [B,Hkv,Lkv,Dv]."""
     B, Hq, Lq, D = _shape4(q, "q")
     Bk, Hkv, Lkv, Dk = _shape4(k, "k")
-    if tuple(v.shape) != tuple(k.shape):
-        raise ValueError(f"v shape {tuple(v.shape)} != k shape {tuple(k.shape)}")
+    Bv, Hv, Lv, Dv = _shape4(v, "v")
+    if (Bv, Hv, Lv) != (Bk, Hkv, Lkv):
+        raise ValueError(f"v shape {tuple(v.shape)} must match k shape {tuple(k.shape)} except in the head dim")
     if Bk != B or Dk != D:
         raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree on batch or head dim")
-    return B, Hq, Hkv, Lq, Lkv, D
+    return B, Hq, Hkv, Lq, Lkv, D, Dv
 
 
 def _mask_args(mask, B, Hq, Lq, Lkv, dev):
@@ -163,22 +169,44 @@ def _mask_args(mask, B, Hq, Lq, Lkv, dev):
     return mask.data_ptr(), int(msb), int(msh)
 
 
+class FaAttnDesc(ctypes.Structure):
+    """fa_attn_desc_t of include/fa.h (the extended calls)."""
+
+    _fields_ = [("B", ctypes.c_int), ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int), ("Lq", ctypes.c_int),
+                ("Lkv", ctypes.c_int), ("D", ctypes.c_int), ("Dv", ctypes.c_int), ("scale", ctypes.c_float),
+                ("causal", ctypes.c_int), ("window", ctypes.c_int), ("mask", ctypes.c_void_p),
+                ("mask_stride_b", ctypes.c_longlong), ("mask_stride_h", ctypes.c_longlong)]
+
+
+def _desc(dims, scale, causal, window, margs):
+    B, Hq, Hkv, Lq, Lkv, D, Dv = dims
+    ptr, msb, msh = margs if margs is not None else (None, 0, 0)
+    return FaAttnDesc(B, Hq, Hkv, Lq, Lkv, D, Dv, float(scale), int(bool(causal)), int(window), ptr, msb, msh)
+
+
 def fa_fwd(q, k, v, o, lse, scale, causal=False, window=0, mask=None):
-    """O and LSE of softmax attention (see include/fa.h, fa_fwd / fa_fwd_masked)."""
+    """O and LSE of softmax attention (see include/fa.h: fa_fwd, or fa_fwd_masked
+    with a mask, or fa_fwd_ex when v's head dim differs from q's)."""
     lib = load_library()
-    B, Hq, Hkv, Lq, Lkv, D = _attn_shapes(q, k, v)
     import torch
 
+    dims = _attn_shapes(q, k, v)
+    B, Hq, Hkv, Lq, Lkv, D, Dv = dims
     dev, dt = q.device, q.dtype
-    if tuple(o.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, Lq):
-        raise ValueError("o must match q and lse must be [B, Hq, Lq]")
+    if tuple(o.shape) != (B, Hq, Lq, Dv) or tuple(lse.shape) != (B, Hq, Lq):
+        raise ValueError("o must be [B, Hq, Lq, Dv] and lse [B, Hq, Lq]")
     ins = (_ptr(q, "q", dev, dt), _ptr(k, "k", dev, dt), _ptr(v, "v", dev, dt))
     outs = (_ptr(o, "o", dev, dt), _ptr(lse, "lse", dev, torch.float32))
+    margs = None if mask is None else _mask_args(mask, B, Hq, Lq, Lkv, dev)
+    if Dv != D:
+        desc = _desc(dims, scale, causal, window, margs)
+        _check("fa_fwd_ex", lib.fa_fwd_ex(ctypes.byref(desc), *ins, *outs, _dtype_code(q), _stream(dev)))
+        return
     rest = (B, Hq, Hkv, Lq, Lkv, D, float(scale), int(bool(causal)), int(window), _dtype_code(q), _stream(dev))
     if mask is None:
         _check("fa_fwd", lib.fa_fwd(*ins, *outs, *rest))
     else:
-        _check("fa_fwd_masked", lib.fa_fwd_masked(*ins, *_mask_args(mask, B, Hq, Lq, Lkv, dev), *outs, *rest))
+        _check("fa_fwd_masked", lib.fa_fwd_masked(*ins, *margs, *outs, *rest))
 
 
 def fa_bwd_preprocess(o, do, delta):
@@ -198,45 +226,55 @@ def fa_bwd_preprocess(o, do, delta):
 def _bwd_common(q, k, v, do, lse, delta):
     import torch
 
-    B, Hq, Hkv, Lq, Lkv, D = _attn_shapes(q, k, v)
-    if tuple(do.shape) != tuple(q.shape):
-        raise ValueError("dO must match q")
+    dims = _attn_shapes(q, k, v)
+    B, Hq, Hkv, Lq, Lkv, D, Dv = dims
+    if tuple(do.shape) != (B, Hq, Lq, Dv):
+        raise ValueError("dO must be [B, Hq, Lq, Dv]")
     if tuple(lse.shape) != (B, Hq, Lq) or tuple(delta.shape) != (B, Hq, Lq):
         raise ValueError("lse and delta must be [B, Hq, Lq]")
     dev, dt = q.device, q.dtype
     ptrs = [_ptr(q, "q", dev, dt), _ptr(k, "k", dev, dt), _ptr(v, "v", dev, dt), _ptr(do, "dO", dev, dt),
             _ptr(lse, "lse", dev, torch.float32), _ptr(delta, "delta", dev, torch.float32)]
-    return (B, Hq, Hkv, Lq, Lkv, D), ptrs, dev, dt
+    return dims, ptrs, dev, dt
 
 
 def fa_bwd_dkv(q, k, v, do, lse, delta, dk, dv, scale, causal=False, window=0, mask=None):
-    """dK and dV (see include/fa.h, fa_bwd_dkv / fa_bwd_dkv_masked)."""
+    """dK and dV (see include/fa.h: fa_bwd_dkv, fa_bwd_dkv_masked, fa_bwd_dkv_ex)."""
     lib = load_library()
     dims, ptrs, dev, dt = _bwd_common(q, k, v, do, lse, delta)
-    if tuple(dk.shape) != tuple(k.shape) or tuple(dv.shape) != tuple(k.shape):
-        raise ValueError("dk and dv must match k")
+    B, Hq, Hkv, Lq, Lkv, D, Dv = dims
+    if tuple(dk.shape) != tuple(k.shape) or tuple(dv.shape) != tuple(v.shape):
+        raise ValueError("dk must match k and dv must match v")
     outs = (_ptr(dk, "dk", dev, dt), _ptr(dv, "dv", dev, dt))
-    rest = (*dims, float(scale), int(bool(causal)), int(window), _dtype_code(q), _stream(dev))
+    margs = None if mask is None else _mask_args(mask, B, Hq, Lq, Lkv, dev)
+    if Dv != D:
+        desc = _desc(dims, scale, causal, window, margs)
+        _check("fa_bwd_dkv_ex", lib.fa_bwd_dkv_ex(ctypes.byref(desc), *ptrs, *outs, _dtype_code(q), _stream(dev)))
+        return
+    rest = (B, Hq, Hkv, Lq, Lkv, D, float(scale), int(bool(causal)), int(window), _dtype_code(q), _stream(dev))
     if mask is None:
         _check("fa_bwd_dkv", lib.fa_bwd_dkv(*ptrs, *outs, *rest))
     else:
-        B, Hq, _, Lq, Lkv, _ = dims
-        margs = _mask_args(mask, B, Hq, Lq, Lkv, dev)
         _check("fa_bwd_dkv_masked", lib.fa_bwd_dkv_masked(*ptrs, *margs, *outs, *rest))
 
 
 def fa_bwd_dq(q, k, v, do, lse, delta, dq, scale, causal=False, window=0, mask=None):
-    """dQ (see include/fa.h, fa_bwd_dq / fa_bwd_dq_masked)."""
+    """dQ (see include/fa.h: fa_bwd_dq, fa_bwd_dq_masked, fa_bwd_dq_ex)."""
     lib = load_library()
     dims, ptrs, dev, dt = _bwd_common(q, k, v, do, lse, delta)
+    B, Hq, Hkv, Lq, Lkv, D, Dv = dims
     if tuple(dq.shape) != tuple(q.shape):
         raise ValueError("dq must match q")
-    rest = (*dims, float(scale), int(bool(causal)), int(window), _dtype_code(q), _stream(dev))
+    margs = None if mask is None else _mask_args(mask, B, Hq, Lq, Lkv, dev)
+    if Dv != D:
+        desc = _desc(dims, scale, causal, window, margs)
+        _check("fa_bwd_dq_ex", lib.fa_bwd_dq_ex(ctypes.byref(desc), *ptrs, _ptr(dq, "dq", dev, dt), _dtype_code(q),
+                                                _stream(dev)))
+        return
+    rest = (B, Hq, Hkv, Lq, Lkv, D, float(scale), int(bool(causal)), int(window), _dtype_code(q), _stream(dev))
     if mask is None:
         _check("fa_bwd_dq", lib.fa_bwd_dq(*ptrs, _ptr(dq, "dq", dev, dt), *rest))
     else:
-        B, Hq, _, Lq, Lkv, _ = dims
-        margs = _mask_args(mask, B, Hq, Lq, Lkv, dev)
         _check("fa_bwd_dq_masked", lib.fa_bwd_dq_masked(*ptrs, *margs, _ptr(dq, "dq", dev, dt), *rest))
 
 
@@ -249,7 +287,7 @@ def forward(q, k, v, scale=None, causal=False, window=0, mask=None):
     import torch
 
     B, Hq, Lq, D = q.shape
-    o = torch.empty_like(q)
+    o = torch.empty((B, Hq, Lq, v.shape[-1]), device=q.device, dtype=q.dtype)
     lse = torch.empty((B, Hq, Lq), device=q.device, dtype=torch.float32)
     fa_fwd(q, k, v, o, lse, default_scale(D) if scale is None else scale, causal, window, mask)
     return o, lse

@@ -42,18 +42,20 @@ def unsupported_reason(q, k, v, window: int = 0) -> str | None:
         return "q, k, v are on different devices"
     B, Hq, Lq, D = q.shape
     Bk, Hkv, Lkv, Dk = k.shape
-    if tuple(v.shape) != tuple(k.shape):
-        return f"v shape {tuple(v.shape)} differs from k shape {tuple(k.shape)}"
+    Dv = v.shape[3]
+    if tuple(v.shape[:3]) != tuple(k.shape[:3]):
+        return f"v shape {tuple(v.shape)} differs from k shape {tuple(k.shape)} outside the head dim"
     if Bk != B or Dk != D:
         return f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree on batch or head dim"
     if min(B, Hq, Hkv, Lq, Lkv) <= 0:
         return "empty dimension"
     if Hq % Hkv:
         return f"Hq={Hq} is not a multiple of Hkv={Hkv}"
-    if D % 8 or D < 32 or D > 512:
-        return f"head dim {D} outside the supported set (multiple of 8 in [32, 512])"
-    if q.dtype == torch.float32 and D > 256:
-        return f"float32 inputs support head dim up to 256, got {D}"
+    for name, d in (("head dim", D), ("value head dim", Dv)):
+        if d % 8 or d < 32 or d > 512:
+            return f"{name} {d} outside the supported set (multiple of 8 in [32, 512])"
+        if q.dtype == torch.float32 and d > 256:
+            return f"float32 inputs support a {name} up to 256, got {d}"
     if window < 0:
         return f"window must be >= 0, got {window}"
     return None
@@ -86,7 +88,8 @@ def flash_attention(q, k, v, scale: float | None = None, causal: bool = False, w
                     return_lse: bool = False, mask=None):
     """Differentiable softmax(scale * q k^T + mask) v on the HIP kernels.
 
-    q: [B, Hq, Lq, D]; k, v: [B, Hkv, Lkv, D] (Hq a multiple of Hkv); one of
+    q: [B, Hq, Lq, D]; k: [B, Hkv, Lkv, D]; v: [B, Hkv, Lkv, Dv] (Hq a multiple
+    of Hkv; O is [B, Hq, Lq, Dv]); one of
     float32 / float16 / bfloat16 on one GPU. scale defaults to 1/sqrt(D).
     causal: key j is allowed for query i only if j <= i (top-left aligned).
     window > 0: additionally only keys with i - j < window (plus, without

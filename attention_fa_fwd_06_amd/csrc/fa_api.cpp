@@ -43,6 +43,16 @@ fa_status_t check_attn(int B, int Hq, int Hkv, int Lq, int Lkv, int D, float sca
     return FA_OK;
 }
 
+// The value head dim of the extended calls: the same rules as D, and the same
+// size limits for the tensors that carry it (v, o, dO, dV).
+fa_status_t check_dv(int B, int Hq, int Hkv, int Lq, int Lkv, int Dv, fa_dtype_t dt) {
+    fa_status_t st = check_headdim(Dv, dt);
+    if (st != FA_OK) return st;
+    if ((long long)B * Hq * Lq * Dv > kMaxElems || (long long)B * Hkv * Lkv * Dv > kMaxElems) return FA_ERR_SHAPE;
+    if ((long long)Lq * Dv > kMaxHeadElems || (long long)Lkv * Dv > kMaxHeadElems) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
 fa_status_t from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
 
 // Mask tensor of the masked entry points: non-NULL, 4-byte aligned, strides
@@ -85,17 +95,19 @@ const char* fa_status_string(fa_status_t s) {
 
 static fa_status_t fwd_impl(const void* q, const void* k, const void* v, const float* mask, long long msb,
                             long long msh, void* o, float* lse, int B, int Hq, int Hkv, int Lq, int Lkv, int D,
-                            float scale, int causal, int window, fa_dtype_t dtype, void* stream) {
+                            int Dv, float scale, int causal, int window, fa_dtype_t dtype, void* stream) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     fa_status_t st = check_dtype(dtype);
     if (st != FA_OK) return st;
     st = check_attn(B, Hq, Hkv, Lq, Lkv, D, scale, window, dtype);
     if (st != FA_OK) return st;
+    st = check_dv(B, Hq, Hkv, Lq, Lkv, Dv, dtype);
+    if (st != FA_OK) return st;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
 
     fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Lq, Lkv, D,
                   (float)((double)scale * 1.4426950408889634), causal ? 1 : 0, effective_window(window, Lq),
-                  mask, msb, msh, mask ? mask_vec4(mask, msb, msh, Lkv) : 0};
+                  mask, msb, msh, mask ? mask_vec4(mask, msb, msh, Lkv) : 0, Dv};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     switch (dtype) {
         case FA_F32: return from_hip(fa::launch_fwd_f32(a, s));
@@ -107,7 +119,7 @@ static fa_status_t fwd_impl(const void* q, const void* k, const void* v, const f
 
 fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                    int Lq, int Lkv, int D, float scale, int causal, int window, fa_dtype_t dtype, void* stream) {
-    return fwd_impl(q, k, v, nullptr, 0, 0, o, lse, B, Hq, Hkv, Lq, Lkv, D, scale, causal, window, dtype, stream);
+    return fwd_impl(q, k, v, nullptr, 0, 0, o, lse, B, Hq, Hkv, Lq, Lkv, D, D, scale, causal, window, dtype, stream);
 }
 
 fa_status_t fa_fwd_masked(const void* q, const void* k, const void* v, const float* mask, long long mask_stride_b,
@@ -115,7 +127,7 @@ fa_status_t fa_fwd_masked(const void* q, const void* k, const void* v, const flo
                           int D, float scale, int causal, int window, fa_dtype_t dtype, void* stream) {
     fa_status_t st = check_mask(mask, mask_stride_b, mask_stride_h);
     if (st != FA_OK) return st;
-    return fwd_impl(q, k, v, mask, mask_stride_b, mask_stride_h, o, lse, B, Hq, Hkv, Lq, Lkv, D, scale, causal,
+    return fwd_impl(q, k, v, mask, mask_stride_b, mask_stride_h, o, lse, B, Hq, Hkv, Lq, Lkv, D, D, scale, causal,
                     window, dtype, stream);
 }
 
@@ -141,12 +153,14 @@ fa_status_t fa_bwd_preprocess(const void* o, const void* dO, float* delta, int B
 }
 
 static fa_status_t bwd_common(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                              const float* delta, int B, int Hq, int Hkv, int Lq, int Lkv, int D, float scale,
-                              int window, fa_dtype_t dtype) {
+                              const float* delta, int B, int Hq, int Hkv, int Lq, int Lkv, int D, int Dv,
+                              float scale, int window, fa_dtype_t dtype) {
     if (!q || !k || !v || !dO || !lse || !delta) return FA_ERR_NULL;
     fa_status_t st = check_dtype(dtype);
     if (st != FA_OK) return st;
     st = check_attn(B, Hq, Hkv, Lq, Lkv, D, scale, window, dtype);
+    if (st != FA_OK) return st;
+    st = check_dv(B, Hq, Hkv, Lq, Lkv, Dv, dtype);
     if (st != FA_OK) return st;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(lse) || !aligned16(delta))
         return FA_ERR_ALIGN;
@@ -155,16 +169,16 @@ static fa_status_t bwd_common(const void* q, const void* k, const void* v, const
 
 static fa_status_t dkv_impl(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                             const float* delta, const float* mask, long long msb, long long msh, void* dk, void* dv,
-                            int B, int Hq, int Hkv, int Lq, int Lkv, int D, float scale, int causal, int window,
-                            fa_dtype_t dtype, void* stream) {
+                            int B, int Hq, int Hkv, int Lq, int Lkv, int D, int Dv, float scale, int causal,
+                            int window, fa_dtype_t dtype, void* stream) {
     if (!dk || !dv) return FA_ERR_NULL;
-    fa_status_t st = bwd_common(q, k, v, dO, lse, delta, B, Hq, Hkv, Lq, Lkv, D, scale, window, dtype);
+    fa_status_t st = bwd_common(q, k, v, dO, lse, delta, B, Hq, Hkv, Lq, Lkv, D, Dv, scale, window, dtype);
     if (st != FA_OK) return st;
     if (!aligned16(dk) || !aligned16(dv)) return FA_ERR_ALIGN;
 
     fa::BwdArgs a{q, k, v, dO, lse, delta, nullptr, dk, dv, B, Hq, Hkv, Lq, Lkv, D,
                   (float)((double)scale * 1.4426950408889634), scale, causal ? 1 : 0,
-                  effective_window(window, Lq), mask, msb, msh, mask ? mask_vec4(mask, msb, msh, Lkv) : 0};
+                  effective_window(window, Lq), mask, msb, msh, mask ? mask_vec4(mask, msb, msh, Lkv) : 0, Dv};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     switch (dtype) {
         case FA_F32: return from_hip(fa::launch_dkv_f32(a, s));
@@ -177,7 +191,7 @@ static fa_status_t dkv_impl(const void* q, const void* k, const void* v, const v
 fa_status_t fa_bwd_dkv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                        const float* delta, void* dk, void* dv, int B, int Hq, int Hkv, int Lq, int Lkv, int D,
                        float scale, int causal, int window, fa_dtype_t dtype, void* stream) {
-    return dkv_impl(q, k, v, dO, lse, delta, nullptr, 0, 0, dk, dv, B, Hq, Hkv, Lq, Lkv, D, scale, causal, window,
+    return dkv_impl(q, k, v, dO, lse, delta, nullptr, 0, 0, dk, dv, B, Hq, Hkv, Lq, Lkv, D, D, scale, causal, window,
                     dtype, stream);
 }
 
@@ -187,22 +201,22 @@ fa_status_t fa_bwd_dkv_masked(const void* q, const void* k, const void* v, const
                               int D, float scale, int causal, int window, fa_dtype_t dtype, void* stream) {
     fa_status_t st = check_mask(mask, mask_stride_b, mask_stride_h);
     if (st != FA_OK) return st;
-    return dkv_impl(q, k, v, dO, lse, delta, mask, mask_stride_b, mask_stride_h, dk, dv, B, Hq, Hkv, Lq, Lkv, D,
+    return dkv_impl(q, k, v, dO, lse, delta, mask, mask_stride_b, mask_stride_h, dk, dv, B, Hq, Hkv, Lq, Lkv, D, D,
                     scale, causal, window, dtype, stream);
 }
 
 static fa_status_t dq_impl(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                            const float* delta, const float* mask, long long msb, long long msh, void* dq, int B,
-                           int Hq, int Hkv, int Lq, int Lkv, int D, float scale, int causal, int window,
+                           int Hq, int Hkv, int Lq, int Lkv, int D, int Dv, float scale, int causal, int window,
                            fa_dtype_t dtype, void* stream) {
     if (!dq) return FA_ERR_NULL;
-    fa_status_t st = bwd_common(q, k, v, dO, lse, delta, B, Hq, Hkv, Lq, Lkv, D, scale, window, dtype);
+    fa_status_t st = bwd_common(q, k, v, dO, lse, delta, B, Hq, Hkv, Lq, Lkv, D, Dv, scale, window, dtype);
     if (st != FA_OK) return st;
     if (!aligned16(dq)) return FA_ERR_ALIGN;
 
     fa::BwdArgs a{q, k, v, dO, lse, delta, dq, nullptr, nullptr, B, Hq, Hkv, Lq, Lkv, D,
                   (float)((double)scale * 1.4426950408889634), scale, causal ? 1 : 0,
-                  effective_window(window, Lq), mask, msb, msh, mask ? mask_vec4(mask, msb, msh, Lkv) : 0};
+                  effective_window(window, Lq), mask, msb, msh, mask ? mask_vec4(mask, msb, msh, Lkv) : 0, Dv};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     switch (dtype) {
         case FA_F32: return from_hip(fa::launch_dq_f32(a, s));
@@ -215,7 +229,7 @@ static fa_status_t dq_impl(const void* q, const void* k, const void* v, const vo
 fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                       const float* delta, void* dq, int B, int Hq, int Hkv, int Lq, int Lkv, int D, float scale,
                       int causal, int window, fa_dtype_t dtype, void* stream) {
-    return dq_impl(q, k, v, dO, lse, delta, nullptr, 0, 0, dq, B, Hq, Hkv, Lq, Lkv, D, scale, causal, window, dtype,
+    return dq_impl(q, k, v, dO, lse, delta, nullptr, 0, 0, dq, B, Hq, Hkv, Lq, Lkv, D, D, scale, causal, window, dtype,
                    stream);
 }
 
@@ -225,8 +239,40 @@ fa_status_t fa_bwd_dq_masked(const void* q, const void* k, const void* v, const 
                              int window, fa_dtype_t dtype, void* stream) {
     fa_status_t st = check_mask(mask, mask_stride_b, mask_stride_h);
     if (st != FA_OK) return st;
-    return dq_impl(q, k, v, dO, lse, delta, mask, mask_stride_b, mask_stride_h, dq, B, Hq, Hkv, Lq, Lkv, D, scale,
+    return dq_impl(q, k, v, dO, lse, delta, mask, mask_stride_b, mask_stride_h, dq, B, Hq, Hkv, Lq, Lkv, D, D, scale,
                    causal, window, dtype, stream);
+}
+
+// Extended calls: one descriptor carries the sizes (with a value head dim),
+// the mask flags and the optional mask.
+static fa_status_t check_desc(const fa_attn_desc_t* d) {
+    if (!d) return FA_ERR_NULL;
+    if (d->mask) return check_mask(d->mask, d->mask_stride_b, d->mask_stride_h);
+    return FA_OK;
+}
+
+fa_status_t fa_fwd_ex(const fa_attn_desc_t* d, const void* q, const void* k, const void* v, void* o, float* lse,
+                      fa_dtype_t dtype, void* stream) {
+    fa_status_t st = check_desc(d);
+    if (st != FA_OK) return st;
+    return fwd_impl(q, k, v, d->mask, d->mask_stride_b, d->mask_stride_h, o, lse, d->B, d->Hq, d->Hkv, d->Lq,
+                    d->Lkv, d->D, d->Dv, d->scale, d->causal, d->window, dtype, stream);
+}
+
+fa_status_t fa_bwd_dkv_ex(const fa_attn_desc_t* d, const void* q, const void* k, const void* v, const void* dO,
+                          const float* lse, const float* delta, void* dk, void* dv, fa_dtype_t dtype, void* stream) {
+    fa_status_t st = check_desc(d);
+    if (st != FA_OK) return st;
+    return dkv_impl(q, k, v, dO, lse, delta, d->mask, d->mask_stride_b, d->mask_stride_h, dk, dv, d->B, d->Hq,
+                    d->Hkv, d->Lq, d->Lkv, d->D, d->Dv, d->scale, d->causal, d->window, dtype, stream);
+}
+
+fa_status_t fa_bwd_dq_ex(const fa_attn_desc_t* d, const void* q, const void* k, const void* v, const void* dO,
+                         const float* lse, const float* delta, void* dq, fa_dtype_t dtype, void* stream) {
+    fa_status_t st = check_desc(d);
+    if (st != FA_OK) return st;
+    return dq_impl(q, k, v, dO, lse, delta, d->mask, d->mask_stride_b, d->mask_stride_h, dq, d->B, d->Hq, d->Hkv,
+                   d->Lq, d->Lkv, d->D, d->Dv, d->scale, d->causal, d->window, dtype, stream);
 }
 
 }  // extern "C"

@@ -378,7 +378,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_kernel(FwdArgs a) {
 
     const T* qp = reinterpret_cast<const T*>(a.q) + (size_t)(b * a.Hq + hq) * a.Lq * a.D;
     const T* kp = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + g) * a.Lkv * a.D;
-    const T* vp = reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + g) * a.Lkv * a.D;
+    const T* vp = reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + g) * a.Lkv * a.Dv;
 
     // Q fragments of this wave's 32 rows and d slice (B operand of S^T = K Q^T).
     u32x4 qf[C::NKG];
@@ -517,7 +517,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_kernel(FwdArgs a) {
     if constexpr (C::DB) {
         if (n_t > 0) {
             kt.load(kp, t_lo * BKV, a.Lkv, a.D, tid);
-            vt.load(vp, t_lo * BKV, a.Lkv, a.D, tid);
+            vt.load(vp, t_lo * BKV, a.Lkv, a.Dv, tid);
             kt.store(kb0, C::KSTR, tid);
             vt.store_tr(vb0, C::VSTR, tid);
             __syncthreads();
@@ -527,7 +527,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_kernel(FwdArgs a) {
             const bool next = it + 1 < n_t;
             if (next) {
                 kt.load(kp, (t_lo + it + 1) * BKV, a.Lkv, a.D, tid);
-                vt.load(vp, (t_lo + it + 1) * BKV, a.Lkv, a.D, tid);
+                vt.load(vp, (t_lo + it + 1) * BKV, a.Lkv, a.Dv, tid);
             }
             compute(it, kb0 + cur * C::STAGE, vb0 + cur * C::STAGE);
             if (next) {
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_kernel(FwdArgs a) {
         for (int it = 0; it < n_t; ++it) {
             __syncthreads();
             kt.load(kp, (t_lo + it) * BKV, a.Lkv, a.D, tid);
-            vt.load(vp, (t_lo + it) * BKV, a.Lkv, a.D, tid);
+            vt.load(vp, (t_lo + it) * BKV, a.Lkv, a.Dv, tid);
             kt.store(kb0, C::KSTR, tid);
             vt.store_tr(vb0, C::VSTR, tid);
             __syncthreads();
@@ -551,13 +551,13 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_kernel(FwdArgs a) {
     const float l = l_run + __shfl_xor(l_run, 32);
     if (row < a.Lq) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        T* op = reinterpret_cast<T*>(a.o) + ((size_t)(b * a.Hq + hq) * a.Lq + row) * a.D;
+        T* op = reinterpret_cast<T*>(a.o) + ((size_t)(b * a.Hq + hq) * a.Lq + row) * a.Dv;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
                 const int d = dw * C::DS + 32 * db + 8 * qd + 4 * h;
-                if (d < a.D)
+                if (d < a.Dv)
                     store4<T>(op + d, o[db][4 * qd] * inv, o[db][4 * qd + 1] * inv, o[db][4 * qd + 2] * inv,
                               o[db][4 * qd + 3] * inv);
             }
@@ -646,17 +646,16 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_kernel(BwdArgs a) {
 
     const size_t qoff = (size_t)(b * a.Hq + hq) * a.Lq * a.D;
     const T* qp = reinterpret_cast<const T*>(a.q) + qoff;
-    const T* dop = reinterpret_cast<const T*>(a.dO) + qoff;
+    const T* dop = reinterpret_cast<const T*>(a.dO) + (size_t)(b * a.Hq + hq) * a.Lq * a.Dv;
     const T* kp = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + g) * a.Lkv * a.D;
-    const T* vp = reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + g) * a.Lkv * a.D;
+    const T* vp = reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + g) * a.Lkv * a.Dv;
 
     u32x4 qf[C::NKG], df[C::NKG];
 #pragma unroll
     for (int gi = 0; gi < C::NKG; ++gi) {
         const int c = dw * C::SCH + 2 * gi + h;
-        const bool in = row < a.Lq && c * C::E < a.D;
-        qf[gi] = in ? ld16(qp + (size_t)row * a.D + c * C::E) : zero4();
-        df[gi] = in ? ld16(dop + (size_t)row * a.D + c * C::E) : zero4();
+        qf[gi] = (row < a.Lq && c * C::E < a.D) ? ld16(qp + (size_t)row * a.D + c * C::E) : zero4();
+        df[gi] = (row < a.Lq && c * C::E < a.Dv) ? ld16(dop + (size_t)row * a.Dv + c * C::E) : zero4();
     }
     const size_t lrow = (size_t)(b * a.Hq + hq) * a.Lq + row;
     const float lse2 = row < a.Lq ? (MASK ? lse_l2_masked(a.lse[lrow]) : a.lse[lrow] * kLog2e) : 0.f;
@@ -738,7 +737,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_kernel(BwdArgs a) {
     if constexpr (C::DB) {
         if (n_t > 0) {
             kt.load(kp, t_lo * BKV, a.Lkv, a.D, tid);
-            vt.load(vp, t_lo * BKV, a.Lkv, a.D, tid);
+            vt.load(vp, t_lo * BKV, a.Lkv, a.Dv, tid);
             stage_store(smem);
             __syncthreads();
         }
@@ -747,7 +746,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_kernel(BwdArgs a) {
             const bool next = it + 1 < n_t;
             if (next) {
                 kt.load(kp, (t_lo + it + 1) * BKV, a.Lkv, a.D, tid);
-                vt.load(vp, (t_lo + it + 1) * BKV, a.Lkv, a.D, tid);
+                vt.load(vp, (t_lo + it + 1) * BKV, a.Lkv, a.Dv, tid);
             }
             compute(it, smem + cur * C::STAGE);
             if (next) stage_store(smem + (cur ^ 1) * C::STAGE);
@@ -757,7 +756,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_kernel(BwdArgs a) {
         for (int it = 0; it < n_t; ++it) {
             __syncthreads();
             kt.load(kp, (t_lo + it) * BKV, a.Lkv, a.D, tid);
-            vt.load(vp, (t_lo + it) * BKV, a.Lkv, a.D, tid);
+            vt.load(vp, (t_lo + it) * BKV, a.Lkv, a.Dv, tid);
             stage_store(smem);
             __syncthreads();
             compute(it, smem);
@@ -827,9 +826,9 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_kernel(BwdArgs a) {
     const int j0 = kt_idx * C::BKV;
     const int key = j0 + 32 * kw + ln;
 
-    const size_t kvoff = (size_t)(b * a.Hkv + g) * a.Lkv * a.D;
+    const size_t kvoff = (size_t)(b * a.Hkv + g) * a.Lkv * a.D, kvoff_v = (size_t)(b * a.Hkv + g) * a.Lkv * a.Dv;
     const T* kp = reinterpret_cast<const T*>(a.k) + kvoff;
-    const T* vp = reinterpret_cast<const T*>(a.v) + kvoff;
+    const T* vp = reinterpret_cast<const T*>(a.v) + kvoff_v;
 
     // K and V fragments of this lane's key and this wave's d slice
     // (B operands of S = Q K^T and dP = dO V^T).
@@ -837,9 +836,8 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_kernel(BwdArgs a) {
 #pragma unroll
     for (int gi = 0; gi < C::NKG; ++gi) {
         const int c = dw * C::SCH + 2 * gi + h;
-        const bool in = key < a.Lkv && c * C::E < a.D;
-        kf[gi] = in ? ld16(kp + (size_t)key * a.D + c * C::E) : zero4();
-        vf[gi] = in ? ld16(vp + (size_t)key * a.D + c * C::E) : zero4();
+        kf[gi] = (key < a.Lkv && c * C::E < a.D) ? ld16(kp + (size_t)key * a.D + c * C::E) : zero4();
+        vf[gi] = (key < a.Lkv && c * C::E < a.Dv) ? ld16(vp + (size_t)key * a.Dv + c * C::E) : zero4();
     }
 
     f32x16 dk[C::NDB], dv[C::NDB];
@@ -864,9 +862,9 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_kernel(BwdArgs a) {
     auto load = [&](int it) {
         const int hq = g * reps + it / nqt;
         const int q0 = (qt_lo + it % nqt) * BQ;
-        const size_t qoff = (size_t)(b * a.Hq + hq) * a.Lq * a.D;
-        qtile.load(reinterpret_cast<const T*>(a.q) + qoff, q0, a.Lq, a.D, tid);
-        dtile.load(reinterpret_cast<const T*>(a.dO) + qoff, q0, a.Lq, a.D, tid);
+        const size_t qrow0 = (size_t)(b * a.Hq + hq) * a.Lq;
+        qtile.load(reinterpret_cast<const T*>(a.q) + qrow0 * a.D, q0, a.Lq, a.D, tid);
+        dtile.load(reinterpret_cast<const T*>(a.dO) + qrow0 * a.Dv, q0, a.Lq, a.Dv, tid);
         if (tid < BQ) {
             const int r = q0 + tid;
             const size_t li = (size_t)(b * a.Hq + hq) * a.Lq + r;
@@ -981,18 +979,18 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_kernel(BwdArgs a) {
 
     if (key < a.Lkv) {
         T* kop = reinterpret_cast<T*>(a.dk) + kvoff + (size_t)key * a.D;
-        T* vop = reinterpret_cast<T*>(a.dv) + kvoff + (size_t)key * a.D;
+        T* vop = reinterpret_cast<T*>(a.dv) + kvoff_v + (size_t)key * a.Dv;
         const float sc = a.scale;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
                 const int d = dw * C::DS + 32 * db + 8 * qd + 4 * h;
-                if (d < a.D) {
+                if (d < a.D)
                     store4<T>(kop + d, dk[db][4 * qd] * sc, dk[db][4 * qd + 1] * sc, dk[db][4 * qd + 2] * sc,
                               dk[db][4 * qd + 3] * sc);
+                if (d < a.Dv)
                     store4<T>(vop + d, dv[db][4 * qd], dv[db][4 * qd + 1], dv[db][4 * qd + 2], dv[db][4 * qd + 3]);
-                }
             }
     }
 }

@@ -187,6 +187,18 @@ template <int R, int DMAX, int NW> struct DmaPlan {
 #pragma unroll
         for (int n = 0; n < NIW; ++n) dma16(rs, tile + (w + n * NW) * 1024, voff[n] + add);
     }
+    // the same for a tensor whose row pitch Dx differs from the D of init():
+    // the offsets are recomputed from the lane instead of kept in registers
+    __device__ __forceinline__ static void issue_pitch(rsrc_t rs, char* tile, int row0, int Dx, int w, int lane) {
+#pragma unroll
+        for (int n = 0; n < NIW; ++n) {
+            const int slot = 64 * (w + n * NW) + lane;
+            const int r = slot / NDC, p = slot % NDC;
+            const int c = p ^ swz<DMAX * 2>(r);
+            const uint32_t off = (c * 8 < Dx) ? (uint32_t)(((r + row0) * Dx + c * 8) * 2) : kOob;
+            dma16(rs, tile + (w + n * NW) * 1024, off);
+        }
+    }
 };
 
 // ===========================================================================
@@ -224,14 +236,14 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
     const int hq = g * reps + r;
     const int i0 = qt * C::BQ;
     const int row = i0 + 32 * rw + ln;
-    const int D = a.D;
+    const int D = a.D, Dv = a.Dv;
 
     const size_t qhead = (size_t)(b * a.Hq + hq) * a.Lq * D;
-    const size_t kvhead = (size_t)(b * a.Hkv + g) * a.Lkv * D;
-    const uint32_t kvbytes = (uint32_t)a.Lkv * (uint32_t)D * 2u;
     const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + qhead, (uint32_t)a.Lq * (uint32_t)D * 2u);
-    const rsrc_t rk = make_rsrc(reinterpret_cast<const T*>(a.k) + kvhead, kvbytes);
-    const rsrc_t rv = make_rsrc(reinterpret_cast<const T*>(a.v) + kvhead, kvbytes);
+    const rsrc_t rk = make_rsrc(reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + g) * a.Lkv * D,
+                                (uint32_t)a.Lkv * (uint32_t)D * 2u);
+    const rsrc_t rv = make_rsrc(reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + g) * a.Lkv * Dv,
+                                (uint32_t)a.Lkv * (uint32_t)Dv * 2u);
 
     // Q fragments of this wave's 32 rows and d slice (B operand of S^T = K Q^T);
     // rows past Lq and the head-dim tail read as zero.
@@ -272,7 +284,8 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
     auto issue = [&](int t, auto slot) {
         char* st = smem + decltype(slot)::value * C::STAGEB;
         dma.issue(rk, st, (t_lo + t) * BKV, D, w);
-        dma.issue(rv, st + C::TILEB, (t_lo + t) * BKV, D, w);
+        if (Dv == D) dma.issue(rv, st + C::TILEB, (t_lo + t) * BKV, D, w);
+        else dma.issue_pitch(rv, st + C::TILEB, (t_lo + t) * BKV, Dv, w, lane);
     };
     constexpr int LPT = 2 * DmaPlan<BKV, DMAX, C::NW>::NIW;  // DMA instructions per tile per wave
 
@@ -421,13 +434,13 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
     const float l = l_run + __shfl_xor(l_run, 32);
     if (row < a.Lq) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        T* op = reinterpret_cast<T*>(a.o) + qhead + (size_t)row * D;
+        T* op = reinterpret_cast<T*>(a.o) + ((size_t)(b * a.Hq + hq) * a.Lq + row) * Dv;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
                 const int d = dw * C::DS + 32 * db + 8 * qd + 4 * h;
-                if (d < D)
+                if (d < Dv)
                     store4<T>(op + d, o[db][4 * qd] * inv, o[db][4 * qd + 1] * inv, o[db][4 * qd + 2] * inv,
                               o[db][4 * qd + 3] * inv);
             }
@@ -450,7 +463,9 @@ template <class T, int DMAX, int BKV, int RW, int DW, int NS> struct Dq2Cfg {
     static_assert(NS >= 2 && DMAX % 64 == 0 && DS % 32 == 0, "configuration");
 };
 
-template <class T, int DMAX, int BKV, int RW, int DW, int OCC, int NS, bool MASK>
+// VP: the value head dim differs from D (extended calls); the other
+// instantiation takes Dv = D at compile time.
+template <class T, int DMAX, int BKV, int RW, int DW, int OCC, int NS, bool MASK, bool VP>
 __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a) {
     using C = Dq2Cfg<T, DMAX, BKV, RW, DW, NS>;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -470,24 +485,23 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
     const int hq = g * reps + r;
     const int i0 = qt * C::BQ;
     const int row = i0 + 32 * rw + ln;
-    const int D = a.D;
+    const int D = a.D, Dv = VP ? a.Dv : a.D;
 
     const size_t qhead = (size_t)(b * a.Hq + hq) * a.Lq * D;
-    const size_t kvhead = (size_t)(b * a.Hkv + g) * a.Lkv * D;
-    const uint32_t qbytes = (uint32_t)a.Lq * (uint32_t)D * 2u;
-    const uint32_t kvbytes = (uint32_t)a.Lkv * (uint32_t)D * 2u;
-    const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + qhead, qbytes);
-    const rsrc_t rdo = make_rsrc(reinterpret_cast<const T*>(a.dO) + qhead, qbytes);
-    const rsrc_t rk = make_rsrc(reinterpret_cast<const T*>(a.k) + kvhead, kvbytes);
-    const rsrc_t rv = make_rsrc(reinterpret_cast<const T*>(a.v) + kvhead, kvbytes);
+    const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + qhead, (uint32_t)a.Lq * (uint32_t)D * 2u);
+    const rsrc_t rdo = make_rsrc(reinterpret_cast<const T*>(a.dO) + (size_t)(b * a.Hq + hq) * a.Lq * Dv,
+                                 (uint32_t)a.Lq * (uint32_t)Dv * 2u);
+    const rsrc_t rk = make_rsrc(reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + g) * a.Lkv * D,
+                                (uint32_t)a.Lkv * (uint32_t)D * 2u);
+    const rsrc_t rv = make_rsrc(reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + g) * a.Lkv * Dv,
+                                (uint32_t)a.Lkv * (uint32_t)Dv * 2u);
 
     u32x4 qf[C::NKG], df[C::NKG];
 #pragma unroll
     for (int gi = 0; gi < C::NKG; ++gi) {
         const int c = dw * C::SCH + 2 * gi + h;
-        const uint32_t off = c * 8 < D ? (uint32_t)((row * D + c * 8) * 2) : kOob;
-        qf[gi] = buf_ld16(rq, off);
-        df[gi] = buf_ld16(rdo, off);
+        qf[gi] = buf_ld16(rq, c * 8 < D ? (uint32_t)((row * D + c * 8) * 2) : kOob);
+        df[gi] = buf_ld16(rdo, c * 8 < Dv ? (uint32_t)((row * Dv + c * 8) * 2) : kOob);
     }
     const size_t lrow = (size_t)(b * a.Hq + hq) * a.Lq + row;
     const float lse2 = row < a.Lq ? (MASK ? lse_l2_masked(a.lse[lrow]) : a.lse[lrow] * kLog2e) : 0.f;
@@ -517,7 +531,8 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
     auto issue = [&](int t) {
         char* st = smem + (t % NS) * C::STAGEB;
         dma.issue(rk, st, (t_lo + t) * BKV, D, w);
-        dma.issue(rv, st + C::TILEB, (t_lo + t) * BKV, D, w);
+        if constexpr (VP) dma.issue_pitch(rv, st + C::TILEB, (t_lo + t) * BKV, Dv, w, lane);
+        else dma.issue(rv, st + C::TILEB, (t_lo + t) * BKV, D, w);
     };
     constexpr int LPT = 2 * DmaPlan<BKV, DMAX, C::NW>::NIW;
 
@@ -694,13 +709,12 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_lds_kernel(BwdArgs a
     const int reps = a.Hq / a.Hkv;
     const int j0 = kt_idx * C::BKV;
     const int key = j0 + 32 * kw + ln;
-    const int D = a.D;
+    const int D = a.D, Dv = a.Dv;
 
-    const size_t kvhead = (size_t)(b * a.Hkv + g) * a.Lkv * D;
-    const uint32_t kvbytes = (uint32_t)a.Lkv * (uint32_t)D * 2u;
-    const uint32_t qbytes = (uint32_t)a.Lq * (uint32_t)D * 2u;
-    const rsrc_t rk = make_rsrc(reinterpret_cast<const T*>(a.k) + kvhead, kvbytes);
-    const rsrc_t rv = make_rsrc(reinterpret_cast<const T*>(a.v) + kvhead, kvbytes);
+    const size_t kvhead = (size_t)(b * a.Hkv + g) * a.Lkv * D, kvhead_v = (size_t)(b * a.Hkv + g) * a.Lkv * Dv;
+    const uint32_t qbytes = (uint32_t)a.Lq * (uint32_t)D * 2u, obytes = (uint32_t)a.Lq * (uint32_t)Dv * 2u;
+    const rsrc_t rk = make_rsrc(reinterpret_cast<const T*>(a.k) + kvhead, (uint32_t)a.Lkv * (uint32_t)D * 2u);
+    const rsrc_t rv = make_rsrc(reinterpret_cast<const T*>(a.v) + kvhead_v, (uint32_t)a.Lkv * (uint32_t)Dv * 2u);
 
     // K and V fragments of this lane's key and this wave's d slice
     // (B operands of S = Q K^T and dP = dO V^T).
@@ -708,9 +722,8 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_lds_kernel(BwdArgs a
 #pragma unroll
     for (int gi = 0; gi < C::NKG; ++gi) {
         const int c = dw * C::SCH + 2 * gi + h;
-        const uint32_t off = c * 8 < D ? (uint32_t)((key * D + c * 8) * 2) : kOob;
-        kf[gi] = buf_ld16(rk, off);
-        vf[gi] = buf_ld16(rv, off);
+        kf[gi] = buf_ld16(rk, c * 8 < D ? (uint32_t)((key * D + c * 8) * 2) : kOob);
+        vf[gi] = buf_ld16(rv, c * 8 < Dv ? (uint32_t)((key * Dv + c * 8) * 2) : kOob);
     }
 
     f32x16 dk[C::NDB], dv[C::NDB];
@@ -740,12 +753,12 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_lds_kernel(BwdArgs a
     auto issue = [&](int it) {
         const int hq = g * reps + it / nqt;
         const int q0 = (qt_lo + it % nqt) * BQ;
-        const size_t qhead = (size_t)(b * a.Hq + hq) * a.Lq * D;
-        const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + qhead, qbytes);
-        const rsrc_t rdo = make_rsrc(reinterpret_cast<const T*>(a.dO) + qhead, qbytes);
+        const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + (size_t)(b * a.Hq + hq) * a.Lq * D, qbytes);
+        const rsrc_t rdo = make_rsrc(reinterpret_cast<const T*>(a.dO) + (size_t)(b * a.Hq + hq) * a.Lq * Dv, obytes);
         char* st = smem + (it % NS) * C::STAGEB;
         dma.issue(rq, st, q0, D, w);
-        dma.issue(rdo, st + C::TILEB, q0, D, w);
+        if (Dv == D) dma.issue(rdo, st + C::TILEB, q0, D, w);
+        else dma.issue_pitch(rdo, st + C::TILEB, q0, Dv, w, lane);
         const size_t lhead = (size_t)(b * a.Hq + hq) * a.Lq;
         if (w == 0) {
             const rsrc_t rl = make_rsrc(a.lse + lhead, (uint32_t)a.Lq * 4u);
@@ -867,18 +880,18 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_lds_kernel(BwdArgs a
 
     if (key < a.Lkv) {
         T* kop = reinterpret_cast<T*>(a.dk) + kvhead + (size_t)key * D;
-        T* vop = reinterpret_cast<T*>(a.dv) + kvhead + (size_t)key * D;
+        T* vop = reinterpret_cast<T*>(a.dv) + kvhead_v + (size_t)key * Dv;
         const float sc = a.scale;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
                 const int d = dw * C::DS + 32 * db + 8 * qd + 4 * h;
-                if (d < D) {
+                if (d < D)
                     store4<T>(kop + d, dk[db][4 * qd] * sc, dk[db][4 * qd + 1] * sc, dk[db][4 * qd + 2] * sc,
                               dk[db][4 * qd + 3] * sc);
+                if (d < Dv)
                     store4<T>(vop + d, dv[db][4 * qd], dv[db][4 * qd + 1], dv[db][4 * qd + 2], dv[db][4 * qd + 3]);
-                }
             }
     }
 }
@@ -950,12 +963,12 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
     }
     const int b = bg / a.Hkv, g = bg - b * a.Hkv;
     const int reps = a.Hq / a.Hkv;
-    const int D = a.D;
-    const size_t kvhead = (size_t)(b * a.Hkv + g) * a.Lkv * D;
-    const uint32_t kvbytes = (uint32_t)a.Lkv * (uint32_t)D * 2u;
-    const uint32_t qbytes = (uint32_t)a.Lq * (uint32_t)D * 2u;
+    const int D = a.D, Dv = a.Dv;
+    const size_t kvhead = (size_t)(b * a.Hkv + g) * a.Lkv * D, kvhead_v = (size_t)(b * a.Hkv + g) * a.Lkv * Dv;
+    const uint32_t qbytes = (uint32_t)a.Lq * (uint32_t)D * 2u, obytes = (uint32_t)a.Lq * (uint32_t)Dv * 2u;
     // dV wave: K fragments (B of S = Q K^T); dK wave: V fragments (B of dP = dO V^T)
-    const rsrc_t rkv = make_rsrc(reinterpret_cast<const T*>(vw ? a.k : a.v) + kvhead, kvbytes);
+    const rsrc_t rkv = vw ? make_rsrc(reinterpret_cast<const T*>(a.k) + kvhead, (uint32_t)a.Lkv * (uint32_t)D * 2u)
+                          : make_rsrc(reinterpret_cast<const T*>(a.v) + kvhead_v, (uint32_t)a.Lkv * (uint32_t)Dv * 2u);
 
     TileOffs<C::ROWB> to;
     to.init(lane);
@@ -977,6 +990,8 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
     // same order), so each is register-allocated and scheduled on its own.
     auto run = [&](auto role) {
         constexpr bool V = decltype(role)::value;
+        const int Db = V ? D : Dv;  // head dim of this wave's register operand (K or V)
+        const int Do = V ? Dv : D;  // head dim of its output (dV or dK)
 #pragma unroll 1
         for (int pass = 0; pass < 2; ++pass) {
             const int kt = pass ? kt1 : kt0;
@@ -988,7 +1003,7 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
 #pragma unroll
             for (int gi = 0; gi < C::NKG; ++gi) {
                 const int c = cb + 2 * gi + h;
-                bf[gi] = buf_ld16(rkv, c * 8 < D ? (uint32_t)((key * D + c * 8) * 2) : kOob);
+                bf[gi] = buf_ld16(rkv, c * 8 < Db ? (uint32_t)((key * Db + c * 8) * 2) : kOob);
             }
             f32x16 acc[C::NDB];  // dV^T (dV wave) or dK^T (dK wave)
 #pragma unroll
@@ -1003,13 +1018,14 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
             // tiles in the order (query tile from qt_hi down) x (head of the group)
             int hq_issue = g * reps, qt_issue = qt_hi, slot_issue = 0;
             auto issue = [&]() {
-                const size_t qhead = (size_t)(b * a.Hq + hq_issue) * a.Lq * D;
-                const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + qhead, qbytes);
-                const rsrc_t rdo = make_rsrc(reinterpret_cast<const T*>(a.dO) + qhead, qbytes);
+                const size_t qrow0 = (size_t)(b * a.Hq + hq_issue) * a.Lq;
+                const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + qrow0 * D, qbytes);
+                const rsrc_t rdo = make_rsrc(reinterpret_cast<const T*>(a.dO) + qrow0 * Dv, obytes);
                 char* st = smem + slot_issue * C::STAGEB;
                 const int qrow = qt_issue * BQ;
                 dma.issue(rq, st, qrow, D, w);
-                dma.issue(rdo, st + C::TILEB, qrow, D, w);
+                if (Dv == D) dma.issue(rdo, st + C::TILEB, qrow, D, w);
+                else dma.issue_pitch(rdo, st + C::TILEB, qrow, Dv, w, lane);
                 const size_t lhead = (size_t)(b * a.Hq + hq_issue) * a.Lq;
                 if (w == 0) {
                     const rsrc_t rl = make_rsrc(a.lse + lhead, (uint32_t)a.Lq * 4u);
@@ -1208,14 +1224,14 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
             }
 
             if (key < a.Lkv) {
-                T* op = reinterpret_cast<T*>(V ? a.dv : a.dk) + kvhead + (size_t)key * D;
+                T* op = reinterpret_cast<T*>(V ? a.dv : a.dk) + (V ? kvhead_v : kvhead) + (size_t)key * Do;
                 const float sc = V ? 1.f : a.scale;
 #pragma unroll
                 for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
                     for (int qd = 0; qd < 4; ++qd) {
                         const int d = dw * C::DS + 32 * db + 8 * qd + 4 * h;
-                        if (d < D)
+                        if (d < Do)
                             store4<T>(op + d, acc[db][4 * qd] * sc, acc[db][4 * qd + 1] * sc,
                                       acc[db][4 * qd + 2] * sc, acc[db][4 * qd + 3] * sc);
                     }
@@ -1243,8 +1259,10 @@ hipError_t launch_fwd2(const FwdArgs& a, hipStream_t s) {
 template <class T, int DMAX, int BKV, int RW, int DW, int OCC, int NS>
 hipError_t launch_dq2(const BwdArgs& a, hipStream_t s) {
     using C = Dq2Cfg<T, DMAX, BKV, RW, DW, NS>;
-    auto kern = a.mask ? fa_dq_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS, true>
-                       : fa_dq_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS, false>;
+    auto kern = a.Dv != a.D ? (a.mask ? fa_dq_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS, true, true>
+                                      : fa_dq_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS, false, true>)
+                            : (a.mask ? fa_dq_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS, true, false>
+                                      : fa_dq_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS, false, false>);
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
     const long long grid = (long long)((a.Lq + C::BQ - 1) / C::BQ) * a.B * a.Hq;
@@ -1318,7 +1336,7 @@ inline int dmax16(int D) { return D <= 64 ? 64 : D <= 128 ? 128 : D <= 256 ? 256
 #endif
 
 template <class T> hipError_t launch_fwd16(const FwdArgs& a, hipStream_t s) {
-    switch (dmax16(a.D)) {
+    switch (dmax16(a.D > a.Dv ? a.D : a.Dv)) {
         case 64: return launch_fwd2<T, 64, FA2_FWD_64>(a, s);
         case 128: return launch_fwd2<T, 128, FA2_FWD_128>(a, s);
         case 256: return launch_fwd2<T, 256, FA2_FWD_256>(a, s);
@@ -1326,7 +1344,7 @@ template <class T> hipError_t launch_fwd16(const FwdArgs& a, hipStream_t s) {
     }
 }
 template <class T> hipError_t launch_dq16(const BwdArgs& a, hipStream_t s) {
-    switch (dmax16(a.D)) {
+    switch (dmax16(a.D > a.Dv ? a.D : a.Dv)) {
         case 64: return launch_dq2<T, 64, FA2_DQ_64>(a, s);
         case 128: return launch_dq2<T, 128, FA2_DQ_128>(a, s);
         case 256: return launch_dq2<T, 256, FA2_DQ_256>(a, s);
@@ -1345,7 +1363,7 @@ template <class T> hipError_t launch_dq16(const BwdArgs& a, hipStream_t s) {
 #define FA2_DKVS_256 32, 2, 2, 2, 0
 #endif
 template <class T> hipError_t launch_dkv16(const BwdArgs& a, hipStream_t s) {
-    switch (dmax16(a.D)) {
+    switch (dmax16(a.D > a.Dv ? a.D : a.Dv)) {
         case 64: return launch_dkv_pipe<T, 64, FA2_DKVS_64>(a, s);
         case 128: return launch_dkv_pipe<T, 128, FA2_DKVS_128>(a, s);
         case 256: return launch_dkv_pipe<T, 256, FA2_DKVS_256>(a, s);

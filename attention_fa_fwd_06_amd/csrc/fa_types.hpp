@@ -13,7 +13,7 @@ struct FwdArgs {
     const void* v;
     void* o;
     float* lse;
-    int B, Hq, Hkv, Lq, Lkv, D;
+    int B, Hq, Hkv, Lq, Lkv, D;  // D: query/key head dim
     float c;      // scale * log2(e): scores are handled in the exp2 domain
     int causal;
     int window;
@@ -22,6 +22,7 @@ struct FwdArgs {
     const float* mask;
     long long msb, msh;
     int mvec;     // rows of four keys may be read as one 16-byte load
+    int Dv;       // value head dim (v, o): D unless the extended call sets another
 };
 
 // Backward pre-pass: delta = rowsum(dO * O) over rows of length D.
@@ -52,6 +53,7 @@ struct BwdArgs {
     const float* mask;  // as in FwdArgs
     long long msb, msh;
     int mvec;
+    int Dv;       // value head dim (v, dO, dV)
 };
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);

@@ -7,7 +7,9 @@
  *   fa_bwd_dkv        dK, dV (each workgroup owns a block of K/V rows; no atomics)
  *   fa_bwd_dq         dQ
  * and masked variants of the forward and both backward calls that take an
- * additive mask tensor (fa_fwd_masked, fa_bwd_dkv_masked, fa_bwd_dq_masked).
+ * additive mask tensor (fa_fwd_masked, fa_bwd_dkv_masked, fa_bwd_dq_masked),
+ * and extended variants whose value head dim may differ from the query/key
+ * head dim (fa_fwd_ex, fa_bwd_dkv_ex, fa_bwd_dq_ex).
  *
  * Sources: mlx-bun flash-attention.ts (flashForward and flashBackward host
  * functions and the forward, D pre-pass, dK/dV and dQ shaders); the MLX pull
@@ -164,6 +166,44 @@ fa_status_t fa_bwd_dq_masked(const void* q, const void* k, const void* v, const 
                              long long mask_stride_b, long long mask_stride_h, void* dq,
                              int B, int Hq, int Hkv, int Lq, int Lkv, int D,
                              float scale, int causal, int window, fa_dtype_t dtype, void* stream);
+
+/*
+ * Extended calls: everything the calls above do, described by one struct, plus
+ * a value head dim Dv that may differ from the query/key head dim D (the pages'
+ * Dv != Dk case).
+ *   q, dq       : [B, Hq,  Lq,  D]      k, dk : [B, Hkv, Lkv, D]
+ *   o, dO       : [B, Hq,  Lq,  Dv]     v, dv : [B, Hkv, Lkv, Dv]
+ *   lse, delta  : [B, Hq,  Lq]
+ * fa_bwd_preprocess is called with its D set to Dv. Dv follows the rules of
+ * D (a multiple of 8 in [32, 512], at most 256 for FA_F32, the same size
+ * limits for the tensors that carry it); both head dims are served by the
+ * tile shape of the larger one (the columns past each tensor's own head dim
+ * are zero in the tiles and never stored). mask == NULL means no mask (the
+ * strides are then ignored); otherwise it is read exactly as by the masked
+ * calls. desc == NULL returns FA_ERR_NULL.
+ */
+typedef struct {
+    int B, Hq, Hkv, Lq, Lkv;
+    int D;                      /* query/key head dim */
+    int Dv;                     /* value head dim (v, o, dO, dv) */
+    float scale;
+    int causal;
+    int window;
+    const float* mask;          /* optional additive mask (device pointer) */
+    long long mask_stride_b;    /* element strides of the mask, 0 broadcasts */
+    long long mask_stride_h;
+} fa_attn_desc_t;
+
+fa_status_t fa_fwd_ex(const fa_attn_desc_t* desc, const void* q, const void* k, const void* v,
+                      void* o, float* lse, fa_dtype_t dtype, void* stream);
+
+fa_status_t fa_bwd_dkv_ex(const fa_attn_desc_t* desc, const void* q, const void* k, const void* v,
+                          const void* dO, const float* lse, const float* delta, void* dk, void* dv,
+                          fa_dtype_t dtype, void* stream);
+
+fa_status_t fa_bwd_dq_ex(const fa_attn_desc_t* desc, const void* q, const void* k, const void* v,
+                         const void* dO, const float* lse, const float* delta, void* dq,
+                         fa_dtype_t dtype, void* stream);
 
 /* Static, never-NULL description of a status code. */
 const char* fa_status_string(fa_status_t s);

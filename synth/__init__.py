@@ -102,13 +102,15 @@ def draw(shape, dtype: str, sigma: float, rng: np.random.Generator) -> np.ndarra
     return encode(x, dtype)
 
 
-def make_inputs(B, Hq, Hkv, Lq, Lkv, D, dtype, seed, sigma_qkv=1.0, sigma_do=1.0):
-    """Storage arrays for q, k, v, dO drawn in that order from PCG64(seed)."""
+def make_inputs(B, Hq, Hkv, Lq, Lkv, D, dtype, seed, sigma_qkv=1.0, sigma_do=1.0, Dv=None):
+    """Storage arrays for q, k, v, dO drawn in that order from PCG64(seed);
+    v and dO have head dim Dv (default D)."""
+    Dv = D if Dv is None else Dv
     rng = np.random.Generator(np.random.PCG64(seed))
     q = draw((B, Hq, Lq, D), dtype, sigma_qkv, rng)
     k = draw((B, Hkv, Lkv, D), dtype, sigma_qkv, rng)
-    v = draw((B, Hkv, Lkv, D), dtype, sigma_qkv, rng)
-    do = draw((B, Hq, Lq, D), dtype, sigma_do, rng)
+    v = draw((B, Hkv, Lkv, Dv), dtype, sigma_qkv, rng)
+    do = draw((B, Hq, Lq, Dv), dtype, sigma_do, rng)
     return {"q": q, "k": k, "v": v, "do": do}
 
 

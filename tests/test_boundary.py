@@ -226,3 +226,47 @@ def test_binding_mask_shape_checks(lib):
     m = torch.zeros(64, 64)
     with pytest.raises(ValueError):
         fa._mask_args(m, 1, 4, 64, 64, torch.device("cuda", 0))  # not on the GPU
+
+
+def _desc(**kw):
+    d = dict(B=1, Hq=4, Hkv=2, Lq=64, Lkv=64, D=64, Dv=128, scale=0.125, causal=1, window=0, mask=None,
+             mask_stride_b=0, mask_stride_h=0)
+    d.update(kw)
+    return fa.FaAttnDesc(**d)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Dv=36), HEADDIM),
+    (dict(Dv=520), HEADDIM),
+    (dict(Dv=24), HEADDIM),
+    (dict(D=36), HEADDIM),
+    (dict(Hq=5), SHAPE),
+    (dict(window=-2), ARG),
+    (dict(mask=P + 2), ALIGN),
+    (dict(mask=P, mask_stride_h=-1), ARG),
+    (dict(Lq=(1 << 21) + 8, Lkv=64, Dv=256), SHAPE),
+])
+def test_extended_calls_check_the_descriptor(lib, kw, code):
+    d = ctypes.byref(_desc(**kw))
+    assert lib.fa_fwd_ex(d, P, P, P, P, P, fa.FA_BF16, None) == code
+    assert lib.fa_bwd_dkv_ex(d, P, P, P, P, P, P, P, P, fa.FA_BF16, None) == code
+    assert lib.fa_bwd_dq_ex(d, P, P, P, P, P, P, P, fa.FA_BF16, None) == code
+
+
+def test_extended_calls_null_and_dtype(lib):
+    assert lib.fa_fwd_ex(None, P, P, P, P, P, fa.FA_BF16, None) == NULL
+    assert lib.fa_bwd_dkv_ex(None, P, P, P, P, P, P, P, P, fa.FA_BF16, None) == NULL
+    assert lib.fa_bwd_dq_ex(None, P, P, P, P, P, P, P, fa.FA_BF16, None) == NULL
+    d = ctypes.byref(_desc())
+    assert lib.fa_fwd_ex(d, P, P, None, P, P, fa.FA_BF16, None) == NULL
+    assert lib.fa_bwd_dkv_ex(d, P, P, P, P, P, P, P, None, fa.FA_BF16, None) == NULL
+    assert lib.fa_bwd_dq_ex(d, P, P, P, P, P, P, P, 4, None) == DTYPE
+    d32 = ctypes.byref(_desc(Dv=264))
+    assert lib.fa_fwd_ex(d32, P, P, P, P, P, fa.FA_F32, None) == HEADDIM
+    assert lib.fa_fwd_ex(d32, P + 4, P, P, P, P, fa.FA_F16, None) == ALIGN  # Dv = 264 is fine for 16-bit types
+
+
+def test_descriptor_layout_matches_the_header():
+    # int x7, float, int x2, pointer, long long x2 (C layout: 64 bytes, the pointer at 40)
+    assert ctypes.sizeof(fa.FaAttnDesc) == 64
+    assert fa.FaAttnDesc.mask.offset == 40 and fa.FaAttnDesc.mask_stride_h.offset == 56

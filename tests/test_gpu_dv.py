@@ -1,0 +1,68 @@
+"""GPU parity of a value head dim Dv different from the query/key head dim D
+(the extended calls fa_fwd_ex, fa_bwd_dkv_ex, fa_bwd_dq_ex, reached through the
+binding when v's head dim differs from q's) against the float64 oracle, for
+every dtype and head-dim bucket, with masks, windows and Lq != Lkv, and
+through the autograd node."""
+import numpy as np
+import pytest
+import torch
+
+import attention_fa_fwd_06_amd as fa
+import oracle
+from parity_util import check_finite, gpu_inputs, rel_err, to_f64
+from synth import TOL, decode, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # B, Hq, Hkv, Lq, Lkv, D, Dv, dtype, causal, window, masked
+    (1, 4, 2, 150, 150, 64, 128, "bf16", True, 0, False),
+    (2, 4, 1, 97, 97, 128, 64, "f16", False, 0, False),
+    (1, 2, 2, 70, 90, 32, 96, "f32", True, 0, False),
+    (1, 4, 2, 200, 200, 256, 128, "bf16", True, 48, False),
+    (1, 2, 1, 100, 100, 128, 512, "f16", True, 0, False),
+    (1, 2, 2, 64, 64, 160, 72, "f32", False, 0, False),
+    (1, 4, 4, 120, 120, 64, 192, "bf16", False, 0, True),
+]
+
+
+@pytest.mark.parametrize("n", range(len(CASES)),
+                         ids=["B{}_H{}:{}_L{}x{}_D{}_Dv{}_{}_c{}_w{}_m{}".format(*c) for c in CASES])
+def test_value_head_dim_parity(n):
+    B, Hq, Hkv, Lq, Lkv, D, Dv, dtype, causal, window, masked = CASES[n]
+    scale = 1.0 / np.sqrt(D)
+    x = make_inputs(B, Hq, Hkv, Lq, Lkv, D, dtype, 9000 + n, Dv=Dv)
+    bias = None
+    if masked:
+        rng = np.random.default_rng(9100 + n)
+        bias = rng.standard_normal((Lq, Lkv)).astype(np.float32)
+        bias[rng.random((Lq, Lkv)) < 0.2] = -np.inf
+    ref = oracle.backward(*(decode(x[k], dtype) for k in ("q", "k", "v", "do")), scale, causal, window,
+                          bias=None if bias is None else bias.astype(np.float64))
+    t = gpu_inputs(x, dtype)
+    mask = None if bias is None else torch.from_numpy(bias).cuda()
+    o, lse = fa.forward(t["q"], t["k"], t["v"], scale, causal, window, mask=mask)
+    assert tuple(o.shape) == (B, Hq, Lq, Dv)
+    delta = torch.empty((B, Hq, Lq), device="cuda", dtype=torch.float32)
+    dq, dk, dv = fa.backward(t["q"], t["k"], t["v"], o, lse, t["do"], scale, causal, window, delta=delta, mask=mask)
+    torch.cuda.synchronize()
+    got = to_f64({"O": o, "LSE": lse, "Delta": delta, "dQ": dq, "dK": dk, "dV": dv}, dtype)
+    check_finite(got, ref["LSE"])
+    errs = {k: rel_err(got[k], ref[k]) for k in ("O", "LSE", "Delta", "dQ", "dK", "dV")}
+    assert all(e <= TOL[dtype] for e in errs.values()), errs
+
+
+def test_value_head_dim_through_autograd():
+    from attention_fa_fwd_06_amd.autograd import flash_attention
+
+    dtype, D, Dv = "bf16", 128, 64
+    scale = 1.0 / np.sqrt(D)
+    x = make_inputs(1, 4, 2, 110, 110, D, dtype, 9200, Dv=Dv)
+    ref = oracle.backward(*(decode(x[k], dtype) for k in ("q", "k", "v", "do")), scale, True, 0)
+    t = gpu_inputs(x, dtype)
+    q, k, v = (t[n].clone().requires_grad_() for n in ("q", "k", "v"))
+    o = flash_attention(q, k, v, scale, causal=True)
+    o.backward(t["do"])
+    got = to_f64({"O": o.detach(), "dQ": q.grad, "dK": k.grad, "dV": v.grad}, dtype)
+    errs = {key: rel_err(got[key], ref[key]) for key in got}
+    assert all(e <= TOL[dtype] for e in errs.values()), errs
