@@ -116,6 +116,19 @@ __device__ __forceinline__ void prio_valu() {
     if constexpr (FA2_MFMA_PRIO) __builtin_amdgcn_s_setprio(0);
 }
 
+// Sum of the two 16-bit values packed in `pk`, added to acc (one v_dot2 with
+// ones): the forward's row sum of the probabilities as they enter the MFMA.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+template <class T> __device__ __forceinline__ float add_pair(uint32_t pk, float acc);
+template <> __device__ __forceinline__ float add_pair<__bf16>(uint32_t pk, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), bf16x2{(__bf16)1.f, (__bf16)1.f}, acc,
+                                           false);
+}
+template <> __device__ __forceinline__ float add_pair<_Float16>(uint32_t pk, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), f16x2{(_Float16)1.f, (_Float16)1.f}, acc, false);
+}
+
 template <class T> struct Vec8;
 template <> struct Vec8<__bf16> {
     typedef bf16x8 type;
@@ -307,24 +320,24 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
             {
                 constexpr int FB = C::NKG < 8 ? C::NKG : 8, BPK = C::NKG / FB, NB = C::NKB * BPK;
                 auto load = [&](int k, u32x4 (&f)[FB]) {
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < FB; ++i) f[i] = ld16(kl + to.natural(32 * (k / BPK), (k % BPK) * FB + i, cb));
                 };
                 u32x4 cur[FB];
                 load(0, cur);
                 prio_mfma();
-    #pragma unroll
+#pragma unroll
                 for (int k = 0; k < NB; ++k) {
                     u32x4 nxt[FB];
                     if (k + 1 < NB) load(k + 1, nxt);
                     sched_fence();
                     const int kb = k / BPK, g0 = (k % BPK) * FB;
                     if (g0 == 0) s[kb] = zero16();
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < FB; ++i) Mma<T>::nat(s[kb], cur[i], qf[g0 + i]);
                     sched_fence();
                     if (k + 1 < NB) {
-    #pragma unroll
+#pragma unroll
                         for (int i = 0; i < FB; ++i) cur[i] = nxt[i];
                     }
                 }
@@ -334,12 +347,12 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
             if constexpr (MASK) {
                 // masked entry points: c S + log2(e) mask, from here on in the exp2 domain
                 const float* mb = mask_slice(a.mask, a.msb, a.msh, b, hq);
-    #pragma unroll
+#pragma unroll
                 for (int kb = 0; kb < C::NKB; ++kb)
-    #pragma unroll
+#pragma unroll
                     for (int qd = 0; qd < 4; ++qd) {
                         const f32x4 m4 = mask4_l2(mb, row, t0 + 32 * kb + 8 * qd + 4 * h, a.Lq, a.Lkv, a.mvec);
-    #pragma unroll
+#pragma unroll
                         for (int i = 0; i < 4; ++i) s[kb][4 * qd + i] = fmaf(s[kb][4 * qd + i], c, m4[i]);
                     }
             }
@@ -347,7 +360,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
 
             // V^T fragments of the first output block, in flight during the softmax
             u32x4 vcur[C::NPG];
-    #pragma unroll
+#pragma unroll
             for (int gg = 0; gg < C::NPG; ++gg)
                 vcur[gg] = rd_tr(vl + to.transposed(gg, 0, cb, 0), vl + to.transposed(gg, 0, cb, 1));
 
@@ -356,9 +369,9 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
             float mx = -INFINITY;
             if (need) {
                 // key j allowed for this row: j < Lkv and row - j in [dlo, dhi)
-    #pragma unroll
+#pragma unroll
                 for (int kb = 0; kb < C::NKB; ++kb)
-    #pragma unroll
+#pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int j = t0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3), dd = row - j;
                         const bool ok = (j < a.Lkv) & (dd >= dlo) & (dd < dhi);
@@ -366,9 +379,9 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
                         mx = fmaxf(mx, s[kb][r]);
                     }
             } else {
-    #pragma unroll
+#pragma unroll
                 for (int kb = 0; kb < C::NKB; ++kb)
-    #pragma unroll
+#pragma unroll
                     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
             }
             mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -378,52 +391,59 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
                 const float m_new = upd ? m_tile : m_ref;
                 const float alpha = upd ? fast_exp2(m_ref - m_new) : 1.f;
                 l_run *= alpha;
-    #pragma unroll
+#pragma unroll
                 for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
                 m_ref = m_new;
             }
             const float moff = m_ref == -INFINITY ? 0.f : m_ref;
-            float ls = 0.f;
             if (need) {
-    #pragma unroll
+#pragma unroll
                 for (int kb = 0; kb < C::NKB; ++kb)
-    #pragma unroll
+#pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const float sv = s[kb][r];
                         s[kb][r] = sv == -INFINITY ? 0.f : fast_exp2(fmaf(sv, cs, -moff));
-                        ls += s[kb][r];
                     }
             } else {
-    #pragma unroll
+#pragma unroll
                 for (int kb = 0; kb < C::NKB; ++kb)
-    #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        s[kb][r] = fast_exp2(fmaf(s[kb][r], cs, -moff));
-                        ls += s[kb][r];
-                    }
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(fmaf(s[kb][r], cs, -moff));
             }
-            l_run += ls;
 
             // O^T += V^T P^T, one 32-wide output block at a time; the next block's
-            // fragments are requested before this block's MFMAs
+            // fragments are requested before this block's MFMAs. The row sum l
+            // adds the probabilities as rounded for the MFMA, two per instruction
+            // (the same values that weight V).
             PF<T> pf[C::NPG];
-    #pragma unroll
+#pragma unroll
             for (int gg = 0; gg < C::NPG; ++gg) pf[gg] = make_pf<T>(s[gg >> 1], gg & 1);
+            {
+                float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+                for (int gg = 0; gg < C::NPG; ++gg) {
+                    ls0 = add_pair<T>(pf[gg].v[0], ls0);
+                    ls1 = add_pair<T>(pf[gg].v[1], ls1);
+                    ls0 = add_pair<T>(pf[gg].v[2], ls0);
+                    ls1 = add_pair<T>(pf[gg].v[3], ls1);
+                }
+                l_run += ls0 + ls1;
+            }
             prio_mfma();
-    #pragma unroll
+#pragma unroll
             for (int db = 0; db < C::NDB; ++db) {
                 u32x4 vnxt[C::NPG];
                 if (db + 1 < C::NDB) {
-    #pragma unroll
+#pragma unroll
                     for (int gg = 0; gg < C::NPG; ++gg)
                         vnxt[gg] = rd_tr(vl + to.transposed(gg, db + 1, cb, 0), vl + to.transposed(gg, db + 1, cb, 1));
                 }
                 sched_fence();
-    #pragma unroll
+#pragma unroll
                 for (int gg = 0; gg < C::NPG; ++gg) Mma<T>::nat(o[db], vcur[gg], pf[gg].v);
                 sched_fence();
                 if (db + 1 < C::NDB) {
-    #pragma unroll
+#pragma unroll
                     for (int gg = 0; gg < C::NPG; ++gg) vcur[gg] = vnxt[gg];
                 }
             }
