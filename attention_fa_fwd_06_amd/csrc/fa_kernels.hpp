@@ -1063,85 +1063,42 @@ inline int dmax_bucket(int D) {
     return 512;
 }
 
-// Two waves per SIMD fit the 16-bit kernels' registers; float operands take
-// twice the registers and stay at one.
-template <class T> constexpr int kOcc2 = sizeof(T) == 2 ? 2 : 1;
-// float forward tiles at head dim 96/128 take 32 keys to stay within registers.
-template <class T> constexpr int kFwdBkv = sizeof(T) == 2 ? 64 : 32;
-
-// Tile configuration of the hot head dims: <KV or Q tile, waves along rows or
-// keys, waves along d, minimum waves per SIMD>. Overridable at build time for
-// tuning sweeps of the 16-bit kernels (e.g. -DFA_FWD_128=64,4,1,2).
-#ifndef FA_FWD_128
-#define FA_FWD_128 64, 4, 1, 2
-#endif
-#ifndef FA_DQ_128
-#define FA_DQ_128 32, 4, 1, 2
-#endif
-#ifndef FA_DKV_128
-#define FA_DKV_128 64, 4, 1, 1
-#endif
-#ifndef FA_FWD_256
-#define FA_FWD_256 32, 4, 1, 1
-#endif
-#ifndef FA_DQ_256
-#define FA_DQ_256 32, 4, 1, 1
-#endif
-#ifndef FA_DKV_256
-#define FA_DKV_256 64, 2, 2, 1
-#endif
-
-// Head dims up to 128 run one wave per d range; 256 and 512 split d in
-// slices of 128 over DW waves. float inputs stop at head dim 256: their
-// staged Q, dO, Q^T and dO^T tiles at 512 exceed the 160 KB of LDS.
+// float tables (the 16-bit types run the LDS-DMA kernels of fa_kernels_lds.hpp):
+// <KV or Q tile, waves along rows or keys, waves along d, minimum waves per
+// SIMD>. float operands take twice the registers of 16-bit ones, so forward
+// tiles at head dim 96/128 take 32 keys and most tables run one wave per
+// SIMD; 256 splits d in two slices of 128. float inputs stop at head dim 256:
+// their staged Q, dO, Q^T and dO^T tiles at 512 exceed the 160 KB of LDS.
 template <class T> hipError_t launch_fwd_t(int dmax, const FwdArgs& a, hipStream_t s) {
+    static_assert(sizeof(T) == 4, "float tables");
     switch (dmax) {
-        case 32: return launch_fwd_cfg<T, 32, 64, 4, 1, kOcc2<T>>(a, s);
-        case 64: return launch_fwd_cfg<T, 64, 64, 4, 1, kOcc2<T>>(a, s);
-        case 96: return launch_fwd_cfg<T, 96, kFwdBkv<T>, 4, 1, kOcc2<T>>(a, s);
-        case 128:
-            if constexpr (sizeof(T) == 2) return launch_fwd_cfg<T, 128, FA_FWD_128>(a, s);
-            else return launch_fwd_cfg<T, 128, 32, 4, 1, 1>(a, s);
-        case 256:
-            if constexpr (sizeof(T) == 2) return launch_fwd_cfg<T, 256, FA_FWD_256>(a, s);
-            else return launch_fwd_cfg<T, 256, 32, 2, 2, 1>(a, s);
-        case 512:
-            if constexpr (sizeof(T) == 2) return launch_fwd_cfg<T, 512, 32, 1, 4, 1>(a, s);
-            break;
+        case 32: return launch_fwd_cfg<T, 32, 64, 4, 1, 1>(a, s);
+        case 64: return launch_fwd_cfg<T, 64, 64, 4, 1, 1>(a, s);
+        case 96: return launch_fwd_cfg<T, 96, 32, 4, 1, 1>(a, s);
+        case 128: return launch_fwd_cfg<T, 128, 32, 4, 1, 1>(a, s);
+        case 256: return launch_fwd_cfg<T, 256, 32, 2, 2, 1>(a, s);
     }
     return hipErrorInvalidValue;
 }
 template <class T> hipError_t launch_dq_t(int dmax, const BwdArgs& a, hipStream_t s) {
+    static_assert(sizeof(T) == 4, "float tables");
     switch (dmax) {
-        case 32: return launch_dq_cfg<T, 32, 32, 4, 1, kOcc2<T>>(a, s);
-        case 64: return launch_dq_cfg<T, 64, 32, 4, 1, kOcc2<T>>(a, s);
-        case 96: return launch_dq_cfg<T, 96, 32, 4, 1, kOcc2<T>>(a, s);
-        case 128:
-            if constexpr (sizeof(T) == 2) return launch_dq_cfg<T, 128, FA_DQ_128>(a, s);
-            else return launch_dq_cfg<T, 128, 64, 4, 1, 1>(a, s);
-        case 256:
-            if constexpr (sizeof(T) == 2) return launch_dq_cfg<T, 256, FA_DQ_256>(a, s);
-            else return launch_dq_cfg<T, 256, 32, 2, 2, 1>(a, s);
-        case 512:
-            if constexpr (sizeof(T) == 2) return launch_dq_cfg<T, 512, 32, 1, 4, 1>(a, s);
-            break;
+        case 32: return launch_dq_cfg<T, 32, 32, 4, 1, 1>(a, s);
+        case 64: return launch_dq_cfg<T, 64, 32, 4, 1, 1>(a, s);
+        case 96: return launch_dq_cfg<T, 96, 32, 4, 1, 1>(a, s);
+        case 128: return launch_dq_cfg<T, 128, 64, 4, 1, 1>(a, s);
+        case 256: return launch_dq_cfg<T, 256, 32, 2, 2, 1>(a, s);
     }
     return hipErrorInvalidValue;
 }
 template <class T> hipError_t launch_dkv_t(int dmax, const BwdArgs& a, hipStream_t s) {
+    static_assert(sizeof(T) == 4, "float tables");
     switch (dmax) {
         case 32: return launch_dkv_cfg<T, 32, 64, 4, 1, 1>(a, s);
         case 64: return launch_dkv_cfg<T, 64, 64, 4, 1, 1>(a, s);
         case 96: return launch_dkv_cfg<T, 96, 64, 4, 1, 1>(a, s);
-        case 128:
-            if constexpr (sizeof(T) == 2) return launch_dkv_cfg<T, 128, FA_DKV_128>(a, s);
-            else return launch_dkv_cfg<T, 128, 64, 4, 1, 1>(a, s);
-        case 256:
-            if constexpr (sizeof(T) == 2) return launch_dkv_cfg<T, 256, FA_DKV_256>(a, s);
-            else return launch_dkv_cfg<T, 256, 32, 1, 2, 1>(a, s);
-        case 512:
-            if constexpr (sizeof(T) == 2) return launch_dkv_cfg<T, 512, 32, 1, 4, 1>(a, s);
-            break;
+        case 128: return launch_dkv_cfg<T, 128, 64, 4, 1, 1>(a, s);
+        case 256: return launch_dkv_cfg<T, 256, 32, 1, 2, 1>(a, s);
     }
     return hipErrorInvalidValue;
 }
