@@ -1,6 +1,6 @@
 // Kernel instantiations for bf16 inputs (fp32 accumulation): the gfx950
 // LDS-DMA path for the attention kernels, the streaming pre-pass.
-#include "fa_kernels_lds.hpp"
+#include "fa_dispatch16.hpp"
 
 namespace fa {
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) { return lds::launch_fwd16<__bf16>(a, s); }

@@ -1355,22 +1355,6 @@ inline int dmax16(int D) { return D <= 64 ? 64 : D <= 128 ? 128 : D <= 256 ? 256
 #define FA2_DKV_512 32, 1, 4, 1, 2
 #endif
 
-template <class T> hipError_t launch_fwd16(const FwdArgs& a, hipStream_t s) {
-    switch (dmax16(a.D > a.Dv ? a.D : a.Dv)) {
-        case 64: return launch_fwd2<T, 64, FA2_FWD_64>(a, s);
-        case 128: return launch_fwd2<T, 128, FA2_FWD_128>(a, s);
-        case 256: return launch_fwd2<T, 256, FA2_FWD_256>(a, s);
-        default: return launch_fwd2<T, 512, FA2_FWD_512>(a, s);
-    }
-}
-template <class T> hipError_t launch_dq16(const BwdArgs& a, hipStream_t s) {
-    switch (dmax16(a.D > a.Dv ? a.D : a.Dv)) {
-        case 64: return launch_dq2<T, 64, FA2_DQ_64>(a, s);
-        case 128: return launch_dq2<T, 128, FA2_DQ_128>(a, s);
-        case 256: return launch_dq2<T, 256, FA2_DQ_256>(a, s);
-        default: return launch_dq2<T, 512, FA2_DQ_512>(a, s);
-    }
-}
 // dK/dV on wave pairs: <query tile, key blocks of 32, waves splitting d, min waves per SIMD,
 // dV-wave priority>.
 #ifndef FA2_DKVS_64
@@ -1382,14 +1366,6 @@ template <class T> hipError_t launch_dq16(const BwdArgs& a, hipStream_t s) {
 #ifndef FA2_DKVS_256
 #define FA2_DKVS_256 32, 2, 2, 2, 0
 #endif
-template <class T> hipError_t launch_dkv16(const BwdArgs& a, hipStream_t s) {
-    switch (dmax16(a.D > a.Dv ? a.D : a.Dv)) {
-        case 64: return launch_dkv_pipe<T, 64, FA2_DKVS_64>(a, s);
-        case 128: return launch_dkv_pipe<T, 128, FA2_DKVS_128>(a, s);
-        case 256: return launch_dkv_pipe<T, 256, FA2_DKVS_256>(a, s);
-        default: return launch_dkv2<T, 512, FA2_DKV_512>(a, s);
-    }
-}
 
 }  // namespace lds
 }  // namespace fa

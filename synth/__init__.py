@@ -55,6 +55,9 @@ WORKLOADS = [
     Workload("bf16_causal_gqa4_L2048_D128", "bf16", 4, 32, 8, 2048, 2048, 128, True, 0, 1.0, 1.0, TOL["bf16"], 1002),
     Workload("bf16_causal_gqa8_win1024_L8192_D256", "bf16", 1, 16, 2, 8192, 8192, 256, True, 1024, 1.0, 1.0, TOL["bf16"], 1003),
     Workload("bf16_causal_gqa8_L32768_D128", "bf16", 1, 32, 4, 32768, 32768, 128, True, 0, 1.0, 0.01, TOL["bf16"], 1004),
+    # short queries against a long key range (the short-sequence path: 8 query
+    # rows per head, every key visible), the bandwidth-bound case
+    Workload("bf16_gqa4_q8_kv4096_D128", "bf16", 8, 32, 8, 8, 4096, 128, False, 0, 1.0, 1.0, TOL["bf16"], 1005),
 ]
 
 

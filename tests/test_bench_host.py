@@ -48,3 +48,20 @@ def test_traffic_is_reported_only_for_the_kernels_it_was_measured_on(monkeypatch
     monkeypatch.setattr(bench, "kernel_source_digest", lambda: "0" * 64)
     assert bench.measured_traffic("bf16_causal_gqa4_L2048_D128", "fa_bwd_dkv") is None
     assert bench.measured_traffic("no_such_workload", "fa_bwd_dkv") is None
+
+
+def test_roofline_bound_follows_the_machine_balance():
+    # the 2048-token forward: ~815 FLOP per algorithmic byte, above the bf16
+    # balance of 2500 TFLOP/s / 8 TB/s = 312.5 -> matrix-core bound
+    w = WORKLOADS[2]
+    f, by = bench.workload_flops(w), bench.workload_bytes(w)
+    r = bench.roofline("fa_fwd", f["fwd"], by["fwd"], 0.2, bench.PEAK_BF16_TFLOPS)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
+    assert abs(r["achieved"] - f["fwd"] / 0.2e-3 / 1e12) < 1e-9 and abs(r["frac"] - r["achieved"] / 2500) < 1e-12
+    # 8 query rows against 4096 keys: ~32 FLOP per byte -> HBM bound, GB/s
+    w = next(x for x in WORKLOADS if x.name == "bf16_gqa4_q8_kv4096_D128")
+    f, by = bench.workload_flops(w), bench.workload_bytes(w)
+    assert f["fwd"] / by["fwd"] < 100
+    r = bench.roofline("fa_fwd", f["fwd"], by["fwd"], 0.01, bench.PEAK_BF16_TFLOPS)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert abs(r["achieved"] - by["fwd"] / 0.01e-3 / 1e9) < 1e-6
