@@ -42,11 +42,42 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 buf_ld16(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
-__device__ __forceinline__ void dma16(rsrc_t r, char* lds_dst, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_dst, 16, voff, 0, 0, 0);
+
+// HBM -> LDS DMA (buffer_load ... lds) written as assembly. Issued through the
+// compiler's intrinsic, every transposing LDS read (ds_read_b64_tr_b16) that
+// follows a DMA gets an `s_waitcnt vmcnt(0)` in front of it, since the
+// compiler cannot tell which LDS bytes the DMA writes; that wait drains the
+// prefetch of the next tile in the middle of every step. The kernels order
+// the DMA themselves: wait_vm + a barrier before a tile is read, a barrier
+// before its slot is refilled. The descriptor lives in SGPRs (same fields as
+// make_rsrc); M0 holds the wave's LDS destination and is restored afterwards.
+typedef u32x4 dsc_t;
+__device__ __forceinline__ uint32_t uni(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
+__device__ __forceinline__ dsc_t make_dsc(const void* base, uint32_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    return dsc_t{uni((uint32_t)p), uni((uint32_t)(p >> 32) & 0xffffu), uni(bytes), (uint32_t)kBufWord3};
 }
-__device__ __forceinline__ void dma4(rsrc_t r, char* lds_dst, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_dst, 4, voff, 0, 0, 0);
+// LDS byte address of p, a pointer into the dynamic LDS block `base`
+__device__ __forceinline__ uint32_t lds_of(const char* p, const char* base) {
+    return (uint32_t)(uintptr_t)(const lds_void_t*)base + (uint32_t)(p - base);
+}
+__device__ __forceinline__ void dma16(dsc_t d, uint32_t lds_dst, uint32_t voff) {
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "s"(uni(lds_dst)), "v"(voff), "s"(d)
+        : "memory");
+}
+__device__ __forceinline__ void dma4(dsc_t d, uint32_t lds_dst, uint32_t voff) {
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "s"(uni(lds_dst)), "v"(voff), "s"(d)
+        : "memory");
 }
 // Chunk swizzle of row r for a tile of pitch ROWB bytes (LDS of 64 banks x
 // 4 bytes: 256 bytes per cycle). ROWB >= 256: XOR the low 4 chunk bits with
@@ -195,14 +226,14 @@ template <int R, int DMAX, int NW> struct DmaPlan {
         }
     }
     // rows row0.. of the head described by `rs` (row pitch D elements) -> tile
-    __device__ __forceinline__ void issue(rsrc_t rs, char* tile, int row0, int D, int w) const {
+    __device__ __forceinline__ void issue(dsc_t rs, uint32_t tile, int row0, int D, int w) const {
         const uint32_t add = (uint32_t)row0 * (uint32_t)D * 2u;
 #pragma unroll
         for (int n = 0; n < NIW; ++n) dma16(rs, tile + (w + n * NW) * 1024, voff[n] + add);
     }
     // the same for a tensor whose row pitch Dx differs from the D of init():
     // the offsets are recomputed from the lane instead of kept in registers
-    __device__ __forceinline__ static void issue_pitch(rsrc_t rs, char* tile, int row0, int Dx, int w, int lane) {
+    __device__ __forceinline__ static void issue_pitch(dsc_t rs, uint32_t tile, int row0, int Dx, int w, int lane) {
 #pragma unroll
         for (int n = 0; n < NIW; ++n) {
             const int slot = 64 * (w + n * NW) + lane;
@@ -253,9 +284,9 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
 
     const size_t qhead = (size_t)(b * a.Hq + hq) * a.Lq * D;
     const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + qhead, (uint32_t)a.Lq * (uint32_t)D * 2u);
-    const rsrc_t rk = make_rsrc(reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + g) * a.Lkv * D,
+    const dsc_t rk = make_dsc(reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + g) * a.Lkv * D,
                                 (uint32_t)a.Lkv * (uint32_t)D * 2u);
-    const rsrc_t rv = make_rsrc(reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + g) * a.Lkv * Dv,
+    const dsc_t rv = make_dsc(reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + g) * a.Lkv * Dv,
                                 (uint32_t)a.Lkv * (uint32_t)Dv * 2u);
 
     // Q fragments of this wave's 32 rows and d slice (B operand of S^T = K Q^T);
@@ -296,9 +327,9 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
 
     auto issue = [&](int t, auto slot) {
         char* st = smem + decltype(slot)::value * C::STAGEB;
-        dma.issue(rk, st, (t_lo + t) * BKV, D, w);
-        if (Dv == D) dma.issue(rv, st + C::TILEB, (t_lo + t) * BKV, D, w);
-        else dma.issue_pitch(rv, st + C::TILEB, (t_lo + t) * BKV, Dv, w, lane);
+        dma.issue(rk, lds_of(st, smem), (t_lo + t) * BKV, D, w);
+        if (Dv == D) dma.issue(rv, lds_of(st + C::TILEB, smem), (t_lo + t) * BKV, D, w);
+        else dma.issue_pitch(rv, lds_of(st + C::TILEB, smem), (t_lo + t) * BKV, Dv, w, lane);
     };
     constexpr int LPT = 2 * DmaPlan<BKV, DMAX, C::NW>::NIW;  // DMA instructions per tile per wave
 
@@ -511,9 +542,9 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
     const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + qhead, (uint32_t)a.Lq * (uint32_t)D * 2u);
     const rsrc_t rdo = make_rsrc(reinterpret_cast<const T*>(a.dO) + (size_t)(b * a.Hq + hq) * a.Lq * Dv,
                                  (uint32_t)a.Lq * (uint32_t)Dv * 2u);
-    const rsrc_t rk = make_rsrc(reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + g) * a.Lkv * D,
+    const dsc_t rk = make_dsc(reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + g) * a.Lkv * D,
                                 (uint32_t)a.Lkv * (uint32_t)D * 2u);
-    const rsrc_t rv = make_rsrc(reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + g) * a.Lkv * Dv,
+    const dsc_t rv = make_dsc(reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + g) * a.Lkv * Dv,
                                 (uint32_t)a.Lkv * (uint32_t)Dv * 2u);
 
     u32x4 qf[C::NKG], df[C::NKG];
@@ -550,9 +581,9 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
 
     auto issue = [&](int t) {
         char* st = smem + (t % NS) * C::STAGEB;
-        dma.issue(rk, st, (t_lo + t) * BKV, D, w);
-        if constexpr (VP) dma.issue_pitch(rv, st + C::TILEB, (t_lo + t) * BKV, Dv, w, lane);
-        else dma.issue(rv, st + C::TILEB, (t_lo + t) * BKV, D, w);
+        dma.issue(rk, lds_of(st, smem), (t_lo + t) * BKV, D, w);
+        if constexpr (VP) dma.issue_pitch(rv, lds_of(st + C::TILEB, smem), (t_lo + t) * BKV, Dv, w, lane);
+        else dma.issue(rv, lds_of(st + C::TILEB, smem), (t_lo + t) * BKV, D, w);
     };
     constexpr int LPT = 2 * DmaPlan<BKV, DMAX, C::NW>::NIW;
 
@@ -773,20 +804,20 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_lds_kernel(BwdArgs a
     auto issue = [&](int it) {
         const int hq = g * reps + it / nqt;
         const int q0 = (qt_lo + it % nqt) * BQ;
-        const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + (size_t)(b * a.Hq + hq) * a.Lq * D, qbytes);
-        const rsrc_t rdo = make_rsrc(reinterpret_cast<const T*>(a.dO) + (size_t)(b * a.Hq + hq) * a.Lq * Dv, obytes);
+        const dsc_t rq = make_dsc(reinterpret_cast<const T*>(a.q) + (size_t)(b * a.Hq + hq) * a.Lq * D, qbytes);
+        const dsc_t rdo = make_dsc(reinterpret_cast<const T*>(a.dO) + (size_t)(b * a.Hq + hq) * a.Lq * Dv, obytes);
         char* st = smem + (it % NS) * C::STAGEB;
-        dma.issue(rq, st, q0, D, w);
-        if (Dv == D) dma.issue(rdo, st + C::TILEB, q0, D, w);
-        else dma.issue_pitch(rdo, st + C::TILEB, q0, Dv, w, lane);
+        dma.issue(rq, lds_of(st, smem), q0, D, w);
+        if (Dv == D) dma.issue(rdo, lds_of(st + C::TILEB, smem), q0, D, w);
+        else dma.issue_pitch(rdo, lds_of(st + C::TILEB, smem), q0, Dv, w, lane);
         const size_t lhead = (size_t)(b * a.Hq + hq) * a.Lq;
         if (w == 0) {
-            const rsrc_t rl = make_rsrc(a.lse + lhead, (uint32_t)a.Lq * 4u);
-            if (lane < BQ) dma4(rl, st + 2 * C::TILEB, (uint32_t)(q0 + lane) * 4u);
+            const dsc_t rl = make_dsc(a.lse + lhead, (uint32_t)a.Lq * 4u);
+            if (lane < BQ) dma4(rl, lds_of(st + 2 * C::TILEB, smem), (uint32_t)(q0 + lane) * 4u);
         }
         if (w == WD) {
-            const rsrc_t rd = make_rsrc(a.delta + lhead, (uint32_t)a.Lq * 4u);
-            if (lane < BQ) dma4(rd, st + 2 * C::TILEB + BQ * 4, (uint32_t)(q0 + lane) * 4u);
+            const dsc_t rd = make_dsc(a.delta + lhead, (uint32_t)a.Lq * 4u);
+            if (lane < BQ) dma4(rd, lds_of(st + 2 * C::TILEB + BQ * 4, smem), (uint32_t)(q0 + lane) * 4u);
         }
     };
     constexpr int LPT = 2 * DmaPlan<BQ, DMAX, C::NW>::NIW;
@@ -1039,21 +1070,21 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
             int hq_issue = g * reps, qt_issue = qt_hi, slot_issue = 0;
             auto issue = [&]() {
                 const size_t qrow0 = (size_t)(b * a.Hq + hq_issue) * a.Lq;
-                const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + qrow0 * D, qbytes);
-                const rsrc_t rdo = make_rsrc(reinterpret_cast<const T*>(a.dO) + qrow0 * Dv, obytes);
+                const dsc_t rq = make_dsc(reinterpret_cast<const T*>(a.q) + qrow0 * D, qbytes);
+                const dsc_t rdo = make_dsc(reinterpret_cast<const T*>(a.dO) + qrow0 * Dv, obytes);
                 char* st = smem + slot_issue * C::STAGEB;
                 const int qrow = qt_issue * BQ;
-                dma.issue(rq, st, qrow, D, w);
-                if (Dv == D) dma.issue(rdo, st + C::TILEB, qrow, D, w);
-                else dma.issue_pitch(rdo, st + C::TILEB, qrow, Dv, w, lane);
+                dma.issue(rq, lds_of(st, smem), qrow, D, w);
+                if (Dv == D) dma.issue(rdo, lds_of(st + C::TILEB, smem), qrow, D, w);
+                else dma.issue_pitch(rdo, lds_of(st + C::TILEB, smem), qrow, Dv, w, lane);
                 const size_t lhead = (size_t)(b * a.Hq + hq_issue) * a.Lq;
                 if (w == 0) {
-                    const rsrc_t rl = make_rsrc(a.lse + lhead, (uint32_t)a.Lq * 4u);
-                    if (lane < BQ) dma4(rl, st + 2 * C::TILEB, (uint32_t)(qrow + lane) * 4u);
+                    const dsc_t rl = make_dsc(a.lse + lhead, (uint32_t)a.Lq * 4u);
+                    if (lane < BQ) dma4(rl, lds_of(st + 2 * C::TILEB, smem), (uint32_t)(qrow + lane) * 4u);
                 }
                 if (w == WD) {
-                    const rsrc_t rd = make_rsrc(a.delta + lhead, (uint32_t)a.Lq * 4u);
-                    if (lane < BQ) dma4(rd, st + 2 * C::TILEB + BQ * 4, (uint32_t)(qrow + lane) * 4u);
+                    const dsc_t rd = make_dsc(a.delta + lhead, (uint32_t)a.Lq * 4u);
+                    if (lane < BQ) dma4(rd, lds_of(st + 2 * C::TILEB + BQ * 4, smem), (uint32_t)(qrow + lane) * 4u);
                 }
                 if (++hq_issue == (g + 1) * reps) {
                     hq_issue = g * reps;

@@ -149,9 +149,9 @@ __global__ __launch_bounds__(64 * KW, 1) void fa_fwd_short_kernel(FwdArgs a, Sho
     const int D = a.D, Dv = a.Dv;
 
     const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + R.R0 * D, (uint32_t)R.P * (uint32_t)D * 2u);
-    const rsrc_t rk = make_rsrc(reinterpret_cast<const T*>(a.k) + (size_t)(R.b * a.Hkv + R.g) * a.Lkv * D,
+    const dsc_t rk = make_dsc(reinterpret_cast<const T*>(a.k) + (size_t)(R.b * a.Hkv + R.g) * a.Lkv * D,
                                 (uint32_t)a.Lkv * (uint32_t)D * 2u);
-    const rsrc_t rv = make_rsrc(reinterpret_cast<const T*>(a.v) + (size_t)(R.b * a.Hkv + R.g) * a.Lkv * Dv,
+    const dsc_t rv = make_dsc(reinterpret_cast<const T*>(a.v) + (size_t)(R.b * a.Hkv + R.g) * a.Lkv * Dv,
                                 (uint32_t)a.Lkv * (uint32_t)Dv * 2u);
 
     // Q fragments of the lane's row (B operand of S^T = K Q^T); lanes without
@@ -192,9 +192,9 @@ __global__ __launch_bounds__(64 * KW, 1) void fa_fwd_short_kernel(FwdArgs a, Sho
     auto issue = [&](int t, auto slot) {
         char* st = ring + decltype(slot)::value * C::STAGEB;
         const int r0 = (blo + w + KW * t) * 32;
-        dma.issue(rk, st, r0, D, 0);
-        if (Dv == D) dma.issue(rv, st + C::TILEB, r0, D, 0);
-        else DmaPlan<32, DMAX, 1>::issue_pitch(rv, st + C::TILEB, r0, Dv, 0, lane);
+        dma.issue(rk, lds_of(st, smem), r0, D, 0);
+        if (Dv == D) dma.issue(rv, lds_of(st + C::TILEB, smem), r0, D, 0);
+        else DmaPlan<32, DMAX, 1>::issue_pitch(rv, lds_of(st + C::TILEB, smem), r0, Dv, 0, lane);
     };
     unroll_slots<0, NS - 1>(0, n_w, issue);
 
@@ -355,9 +355,9 @@ __global__ __launch_bounds__(64 * KW, 1) void fa_dq_short_kernel(BwdArgs a, Shor
 
     const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + R.R0 * D, (uint32_t)R.P * (uint32_t)D * 2u);
     const rsrc_t rdo = make_rsrc(reinterpret_cast<const T*>(a.dO) + R.R0 * Dv, (uint32_t)R.P * (uint32_t)Dv * 2u);
-    const rsrc_t rk = make_rsrc(reinterpret_cast<const T*>(a.k) + (size_t)(R.b * a.Hkv + R.g) * a.Lkv * D,
+    const dsc_t rk = make_dsc(reinterpret_cast<const T*>(a.k) + (size_t)(R.b * a.Hkv + R.g) * a.Lkv * D,
                                 (uint32_t)a.Lkv * (uint32_t)D * 2u);
-    const rsrc_t rv = make_rsrc(reinterpret_cast<const T*>(a.v) + (size_t)(R.b * a.Hkv + R.g) * a.Lkv * Dv,
+    const dsc_t rv = make_dsc(reinterpret_cast<const T*>(a.v) + (size_t)(R.b * a.Hkv + R.g) * a.Lkv * Dv,
                                 (uint32_t)a.Lkv * (uint32_t)Dv * 2u);
 
     u32x4 qf[C::NKG], df[C::NKG];
@@ -392,9 +392,9 @@ __global__ __launch_bounds__(64 * KW, 1) void fa_dq_short_kernel(BwdArgs a, Shor
     auto issue = [&](int t, auto slot) {
         char* st = ring + decltype(slot)::value * C::STAGEB;
         const int r0 = (blo + w + KW * t) * 32;
-        dma.issue(rk, st, r0, D, 0);
-        if constexpr (VP) DmaPlan<32, DMAX, 1>::issue_pitch(rv, st + C::TILEB, r0, Dv, 0, lane);
-        else dma.issue(rv, st + C::TILEB, r0, D, 0);
+        dma.issue(rk, lds_of(st, smem), r0, D, 0);
+        if constexpr (VP) DmaPlan<32, DMAX, 1>::issue_pitch(rv, lds_of(st + C::TILEB, smem), r0, Dv, 0, lane);
+        else dma.issue(rv, lds_of(st + C::TILEB, smem), r0, D, 0);
     };
     unroll_slots<0, NS - 1>(0, n_w, issue);
 
@@ -520,10 +520,10 @@ __global__ __launch_bounds__(64 * KW, OCC) void fa_dkv_short_kernel(BwdArgs a) {
     const size_t kvhead = (size_t)(b * a.Hkv + g) * a.Lkv * D, kvhead_v = (size_t)(b * a.Hkv + g) * a.Lkv * Dv;
     const rsrc_t rk = make_rsrc(reinterpret_cast<const T*>(a.k) + kvhead, (uint32_t)a.Lkv * (uint32_t)D * 2u);
     const rsrc_t rv = make_rsrc(reinterpret_cast<const T*>(a.v) + kvhead_v, (uint32_t)a.Lkv * (uint32_t)Dv * 2u);
-    const rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + R0 * D, (uint32_t)P * (uint32_t)D * 2u);
-    const rsrc_t rdo = make_rsrc(reinterpret_cast<const T*>(a.dO) + R0 * Dv, (uint32_t)P * (uint32_t)Dv * 2u);
-    const rsrc_t rl = make_rsrc(a.lse + R0, (uint32_t)P * 4u);
-    const rsrc_t rd = make_rsrc(a.delta + R0, (uint32_t)P * 4u);
+    const dsc_t rq = make_dsc(reinterpret_cast<const T*>(a.q) + R0 * D, (uint32_t)P * (uint32_t)D * 2u);
+    const dsc_t rdo = make_dsc(reinterpret_cast<const T*>(a.dO) + R0 * Dv, (uint32_t)P * (uint32_t)Dv * 2u);
+    const dsc_t rl = make_dsc(a.lse + R0, (uint32_t)P * 4u);
+    const dsc_t rd = make_dsc(a.delta + R0, (uint32_t)P * 4u);
 
     // K and V fragments of the lane's key (B operands of S = Q K^T, dP = dO V^T)
     u32x4 kf[C::NKG], vf[C::NKG];
@@ -549,11 +549,11 @@ __global__ __launch_bounds__(64 * KW, OCC) void fa_dkv_short_kernel(BwdArgs a) {
     constexpr int WD = 1;  // wave 0 fetches lse, wave 1 delta
     auto issue = [&](int it) {
         char* st = smem + (it % NS) * C::STAGEB;
-        dma.issue(rq, st, it * 32, D, w);
-        if (Dv == D) dma.issue(rdo, st + C::TILEB, it * 32, D, w);
-        else DmaPlan<32, DMAX, KW>::issue_pitch(rdo, st + C::TILEB, it * 32, Dv, w, lane);
-        if (w == 0 && lane < 32) dma4(rl, st + 2 * C::TILEB, (uint32_t)(it * 32 + lane) * 4u);
-        if (w == WD && lane < 32) dma4(rd, st + 2 * C::TILEB + 128, (uint32_t)(it * 32 + lane) * 4u);
+        dma.issue(rq, lds_of(st, smem), it * 32, D, w);
+        if (Dv == D) dma.issue(rdo, lds_of(st + C::TILEB, smem), it * 32, D, w);
+        else DmaPlan<32, DMAX, KW>::issue_pitch(rdo, lds_of(st + C::TILEB, smem), it * 32, Dv, w, lane);
+        if (w == 0 && lane < 32) dma4(rl, lds_of(st + 2 * C::TILEB, smem), (uint32_t)(it * 32 + lane) * 4u);
+        if (w == WD && lane < 32) dma4(rd, lds_of(st + 2 * C::TILEB + 128, smem), (uint32_t)(it * 32 + lane) * 4u);
     };
     const int extra = (w == 0) + (w == WD);
 #pragma unroll
