@@ -70,6 +70,17 @@ __device__ __forceinline__ void dma16(dsc_t d, uint32_t lds_dst, uint32_t voff) 
         : "s"(uni(lds_dst)), "v"(voff), "s"(d)
         : "memory");
 }
+// The same with voff (per lane) + add (wave-uniform) formed inside the
+// assembly, so that the compiler keeps no per-tile copies of the lane offsets.
+__device__ __forceinline__ void dma16_add(dsc_t d, uint32_t lds_dst, uint32_t voff, uint32_t add) {
+    uint32_t save, tmp;
+    asm volatile(
+        "v_add_u32 %1, %3, %4\n\ts_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %5, 0 offen lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(save), "=&v"(tmp)
+        : "s"(uni(lds_dst)), "s"(uni(add)), "v"(voff), "s"(d)
+        : "memory");
+}
 __device__ __forceinline__ void dma4(dsc_t d, uint32_t lds_dst, uint32_t voff) {
     uint32_t save;
     asm volatile(
@@ -231,6 +242,11 @@ template <int R, int DMAX, int NW> struct DmaPlan {
 #pragma unroll
         for (int n = 0; n < NIW; ++n) dma16(rs, tile + (w + n * NW) * 1024, voff[n] + add);
     }
+    __device__ __forceinline__ void issue_add(dsc_t rs, uint32_t tile, int row0, int D, int w) const {
+        const uint32_t add = (uint32_t)row0 * (uint32_t)D * 2u;
+#pragma unroll
+        for (int n = 0; n < NIW; ++n) dma16_add(rs, tile + (w + n * NW) * 1024, voff[n], add);
+    }
     // the same for a tensor whose row pitch Dx differs from the D of init():
     // the offsets are recomputed from the lane instead of kept in registers
     __device__ __forceinline__ static void issue_pitch(dsc_t rs, uint32_t tile, int row0, int Dx, int w, int lane) {
@@ -244,6 +260,36 @@ template <int R, int DMAX, int NW> struct DmaPlan {
         }
     }
 };
+
+// max of three scores (v_max3_f32; no NaN arises from the MFMA products)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+// Lane l and lane l^32 of x, as (lower half's value, upper half's value) in
+// every lane: one v_permlane32_swap. (The vector elements are copied out
+// before the bit casts: a bit cast of a vector element subscript reads
+// element 0.)
+__device__ __forceinline__ void halves(float x, float& lo, float& hi) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    lo = __builtin_bit_cast(float, r0);
+    hi = __builtin_bit_cast(float, r1);
+}
+// max over lanes l and l^32 (the same bits in both lanes)
+__device__ __forceinline__ float max_halves(float x) {
+    float lo, hi;
+    halves(x, lo, hi);
+    return fmaxf(lo, hi);
+}
+// sum over lanes l and l^32, added in the same order in both lanes
+__device__ __forceinline__ float sum_halves(float x) {
+    float lo, hi;
+    halves(x, lo, hi);
+    return lo + hi;
+}
 
 // ===========================================================================
 // Forward
@@ -263,7 +309,8 @@ template <class T, int DMAX, int BKV, int RW, int DW, int OCC, int NS, bool MASK
 __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a) {
     using C = Fwd2Cfg<T, DMAX, BKV, RW, DW, NS>;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS DMA destinations depend on it
     const int h = lane >> 5, ln = lane & 31;
     const int rw = w / DW, dw = w % DW;
 
@@ -303,6 +350,11 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
 #pragma unroll
         for (int gi = 0; gi < C::NKG; ++gi) qf[gi] ^= 0x80008000u;
     }
+    // A zero scale becomes 1e-30: every allowed score then enters exp2 within
+    // 1e-25 of the row max, so P is exactly 1 in fp32 as with scale 0, and
+    // -inf (masked) times the factor stays -inf, so exp2 gives exactly 0 with
+    // no further test.
+    c = fmaxf(c, 1e-30f);
 
     f32x16 o[C::NDB];
 #pragma unroll
@@ -321,9 +373,6 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
     dma.init(lane, w, D);
     float* red = reinterpret_cast<float*>(smem + NS * C::STAGEB);
     const int cb = dw * C::SCH;  // chunk base of this wave's d slice
-    // allowed entries: row - key in [dlo, dhi)
-    const int dlo = a.causal ? 0 : INT_MIN;
-    const int dhi = a.window ? a.window : INT_MAX;
 
     auto issue = [&](int t, auto slot) {
         char* st = smem + decltype(slot)::value * C::STAGEB;
@@ -397,26 +446,29 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
 
             const bool need = (t0 + BKV > a.Lkv) || (a.causal && t0 + BKV - 1 > i0) ||
                               (a.window && i_last - t0 >= a.window);
-            float mx = -INFINITY;
             if (need) {
-                // key j allowed for this row: j < Lkv and row - j in [dlo, dhi)
+                // the allowed keys of this lane's row form one run c in [clo, chi]
+                // of the tile offsets c = 32 kb + 8(r/4) + r%4 (key t0 + 4h + c)
+                const int base = row - t0 - 4 * h;
+                int chi = a.Lkv - t0 - 4 * h - 1;
+                if (a.causal) chi = min(chi, base);
+                const int clo = a.window ? base - a.window + 1 : INT_MIN;
 #pragma unroll
                 for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int j = t0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3), dd = row - j;
-                        const bool ok = (j < a.Lkv) & (dd >= dlo) & (dd < dhi);
-                        s[kb][r] = ok ? s[kb][r] : -INFINITY;
-                        mx = fmaxf(mx, s[kb][r]);
+                        const int cr = 32 * kb + 8 * (r >> 2) + (r & 3);
+                        s[kb][r] = (cr >= clo && cr <= chi) ? s[kb][r] : -INFINITY;
                     }
-            } else {
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_tile = mx == -INFINITY ? -INFINITY : mx * cs;
+            constexpr int NSC = 16 * C::NKB;  // scores per lane
+            auto sv = [&](int i) { return s[i / 16][i % 16]; };
+            float mx = max3f(sv(0), sv(1), sv(2));
+#pragma unroll
+            for (int i = 3; i + 1 < NSC; i += 2) mx = max3f(mx, sv(i), sv(i + 1));
+            mx = max3f(mx, sv(NSC - 1), sv(NSC - 1));
+            mx = max_halves(mx);
+            const float m_tile = mx * cs;  // -inf stays -inf (cs > 0)
             const bool upd = m_tile > m_ref + kRescaleLog2;
             if (OCC < 2 || __ballot(upd)) {
                 const float m_new = upd ? m_tile : m_ref;
@@ -427,20 +479,10 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
                 m_ref = m_new;
             }
             const float moff = m_ref == -INFINITY ? 0.f : m_ref;
-            if (need) {
 #pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb)
+            for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float sv = s[kb][r];
-                        s[kb][r] = sv == -INFINITY ? 0.f : fast_exp2(fmaf(sv, cs, -moff));
-                    }
-            } else {
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(fmaf(s[kb][r], cs, -moff));
-            }
+                for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(fmaf(s[kb][r], cs, -moff));
 
             // O^T += V^T P^T, one 32-wide output block at a time; the next block's
             // fragments are requested before this block's MFMAs. The row sum l
@@ -482,7 +524,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
     };
     for (int t = 0; t < n_t; t += NS) unroll_slots<0, NS>(t, n_t, step);
 
-    const float l = l_run + __shfl_xor(l_run, 32);
+    const float l = sum_halves(l_run);
     if (row < a.Lq) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
         T* op = reinterpret_cast<T*>(a.o) + ((size_t)(b * a.Hq + hq) * a.Lq + row) * Dv;
