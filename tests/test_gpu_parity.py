@@ -189,6 +189,17 @@ def test_scale_other_than_default():
     compare_full(1, 4, 2, 100, 100, 64, "bf16", False, 0, seed=24, scale=0.3)
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.2])
+def test_zero_and_negative_scale(scale):
+    # scale 0: every allowed key gets the same weight (O is the mean of the
+    # allowed V rows); a negative scale is folded into Q. Tiled and
+    # short-query paths, causal with a window, ragged lengths.
+    compare_full(1, 4, 2, 150, 150, 128, "bf16", True, 40, seed=26, scale=scale)
+    compare_full(2, 2, 1, 90, 70, 64, "f16", False, 0, seed=27, scale=scale)
+    compare_full(1, 8, 2, 5, 300, 128, "bf16", True, 0, seed=28, scale=scale)
+    compare_full(1, 2, 2, 40, 40, 32, "f32", True, 7, seed=29, scale=scale)
+
+
 def test_deterministic():
     x = make_inputs(1, 8, 2, 300, 300, 128, "bf16", 25)
     t = gpu_inputs(x, "bf16")
