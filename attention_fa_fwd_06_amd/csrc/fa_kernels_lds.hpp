@@ -70,17 +70,6 @@ __device__ __forceinline__ void dma16(dsc_t d, uint32_t lds_dst, uint32_t voff) 
         : "s"(uni(lds_dst)), "v"(voff), "s"(d)
         : "memory");
 }
-// The same with voff (per lane) + add (wave-uniform) formed inside the
-// assembly, so that the compiler keeps no per-tile copies of the lane offsets.
-__device__ __forceinline__ void dma16_add(dsc_t d, uint32_t lds_dst, uint32_t voff, uint32_t add) {
-    uint32_t save, tmp;
-    asm volatile(
-        "v_add_u32 %1, %3, %4\n\ts_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-        "buffer_load_dwordx4 %1, %5, 0 offen lds\n\ts_mov_b32 m0, %0"
-        : "=&s"(save), "=&v"(tmp)
-        : "s"(uni(lds_dst)), "s"(uni(add)), "v"(voff), "s"(d)
-        : "memory");
-}
 __device__ __forceinline__ void dma4(dsc_t d, uint32_t lds_dst, uint32_t voff) {
     uint32_t save;
     asm volatile(
@@ -241,11 +230,6 @@ template <int R, int DMAX, int NW> struct DmaPlan {
         const uint32_t add = (uint32_t)row0 * (uint32_t)D * 2u;
 #pragma unroll
         for (int n = 0; n < NIW; ++n) dma16(rs, tile + (w + n * NW) * 1024, voff[n] + add);
-    }
-    __device__ __forceinline__ void issue_add(dsc_t rs, uint32_t tile, int row0, int D, int w) const {
-        const uint32_t add = (uint32_t)row0 * (uint32_t)D * 2u;
-#pragma unroll
-        for (int n = 0; n < NIW; ++n) dma16_add(rs, tile + (w + n * NW) * 1024, voff[n], add);
     }
     // the same for a tensor whose row pitch Dx differs from the D of init():
     // the offsets are recomputed from the lane instead of kept in registers
