@@ -136,9 +136,10 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 
 // Issue priority around the MFMA chains of the forward and dQ kernels (two
 // workgroups share a CU there): the wave in its product phase goes first, the
-// other wave's softmax VALU fills the issue slots in between.
+// other wave's softmax VALU fills the issue slots in between (measured: D = 256
+// forward about 5 % faster, D = 128 forward and dQ unchanged).
 #ifndef FA2_MFMA_PRIO
-#define FA2_MFMA_PRIO 0
+#define FA2_MFMA_PRIO 1
 #endif
 __device__ __forceinline__ void prio_mfma() {
     if constexpr (FA2_MFMA_PRIO) __builtin_amdgcn_s_setprio(1);
