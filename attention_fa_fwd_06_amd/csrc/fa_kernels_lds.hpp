@@ -1422,7 +1422,7 @@ inline int dmax16(int D) { return D <= 64 ? 64 : D <= 128 ? 128 : D <= 256 ? 256
 #define FA2_DKVS_128 64, 4, 1, 2, 1
 #endif
 #ifndef FA2_DKVS_256
-#define FA2_DKVS_256 32, 2, 2, 2, 0
+#define FA2_DKVS_256 32, 2, 1, 1, 1
 #endif
 
 }  // namespace lds
