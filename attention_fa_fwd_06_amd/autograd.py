@@ -54,8 +54,6 @@ def unsupported_reason(q, k, v, window: int = 0) -> str | None:
     for name, d in (("head dim", D), ("value head dim", Dv)):
         if d % 8 or d < 32 or d > 512:
             return f"{name} {d} outside the supported set (multiple of 8 in [32, 512])"
-        if q.dtype == torch.float32 and d > 256:
-            return f"float32 inputs support a {name} up to 256, got {d}"
     if window < 0:
         return f"window must be >= 0, got {window}"
     return None

@@ -25,17 +25,13 @@ fa_status_t check_dtype(fa_dtype_t dt) {
     return (dt == FA_F32 || dt == FA_F16 || dt == FA_BF16) ? FA_OK : FA_ERR_DTYPE;
 }
 
-fa_status_t check_headdim(int D, fa_dtype_t dt) {
-    if (D < 32 || D > 512 || D % 8 != 0) return FA_ERR_HEADDIM;
-    if (dt == FA_F32 && D > 256) return FA_ERR_HEADDIM;
-    return FA_OK;
-}
+fa_status_t check_headdim(int D) { return (D < 32 || D > 512 || D % 8 != 0) ? FA_ERR_HEADDIM : FA_OK; }
 
-fa_status_t check_attn(int B, int Hq, int Hkv, int Lq, int Lkv, int D, float scale, int window, fa_dtype_t dt) {
+fa_status_t check_attn(int B, int Hq, int Hkv, int Lq, int Lkv, int D, float scale, int window) {
     if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lkv < 1) return FA_ERR_SHAPE;
     if (Hq % Hkv != 0) return FA_ERR_SHAPE;
     if (Lq >= kMaxLen || Lkv >= kMaxLen) return FA_ERR_SHAPE;
-    fa_status_t st = check_headdim(D, dt);
+    fa_status_t st = check_headdim(D);
     if (st != FA_OK) return st;
     if ((long long)B * Hq * Lq * D > kMaxElems || (long long)B * Hkv * Lkv * D > kMaxElems) return FA_ERR_SHAPE;
     if ((long long)Lq * D > kMaxHeadElems || (long long)Lkv * D > kMaxHeadElems) return FA_ERR_SHAPE;
@@ -45,8 +41,8 @@ fa_status_t check_attn(int B, int Hq, int Hkv, int Lq, int Lkv, int D, float sca
 
 // The value head dim of the extended calls: the same rules as D, and the same
 // size limits for the tensors that carry it (v, o, dO, dV).
-fa_status_t check_dv(int B, int Hq, int Hkv, int Lq, int Lkv, int Dv, fa_dtype_t dt) {
-    fa_status_t st = check_headdim(Dv, dt);
+fa_status_t check_dv(int B, int Hq, int Hkv, int Lq, int Lkv, int Dv) {
+    fa_status_t st = check_headdim(Dv);
     if (st != FA_OK) return st;
     if ((long long)B * Hq * Lq * Dv > kMaxElems || (long long)B * Hkv * Lkv * Dv > kMaxElems) return FA_ERR_SHAPE;
     if ((long long)Lq * Dv > kMaxHeadElems || (long long)Lkv * Dv > kMaxHeadElems) return FA_ERR_SHAPE;
@@ -84,7 +80,7 @@ const char* fa_status_string(fa_status_t s) {
         case FA_OK: return "ok";
         case FA_ERR_NULL: return "a required pointer is NULL";
         case FA_ERR_SHAPE: return "bad shape: sizes must be >= 1, Hq a multiple of Hkv, within the size limits";
-        case FA_ERR_HEADDIM: return "head dim must be a multiple of 8 in [32, 512] ([32, 256] for FA_F32)";
+        case FA_ERR_HEADDIM: return "head dim must be a multiple of 8 in [32, 512]";
         case FA_ERR_DTYPE: return "unsupported dtype (FA_F32, FA_F16 or FA_BF16)";
         case FA_ERR_ALIGN: return "every pointer must be 16-byte aligned";
         case FA_ERR_ARG: return "window must be >= 0, scale finite and mask strides in [0, 2^40]";
@@ -99,9 +95,9 @@ static fa_status_t fwd_impl(const void* q, const void* k, const void* v, const f
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     fa_status_t st = check_dtype(dtype);
     if (st != FA_OK) return st;
-    st = check_attn(B, Hq, Hkv, Lq, Lkv, D, scale, window, dtype);
+    st = check_attn(B, Hq, Hkv, Lq, Lkv, D, scale, window);
     if (st != FA_OK) return st;
-    st = check_dv(B, Hq, Hkv, Lq, Lkv, Dv, dtype);
+    st = check_dv(B, Hq, Hkv, Lq, Lkv, Dv);
     if (st != FA_OK) return st;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
 
@@ -137,7 +133,7 @@ fa_status_t fa_bwd_preprocess(const void* o, const void* dO, float* delta, int B
     fa_status_t st = check_dtype(dtype);
     if (st != FA_OK) return st;
     if (B < 1 || Hq < 1 || Lq < 1 || Lq >= kMaxLen) return FA_ERR_SHAPE;
-    st = check_headdim(D, dtype);
+    st = check_headdim(D);
     if (st != FA_OK) return st;
     if ((long long)B * Hq * Lq * D > kMaxElems || (long long)Lq * D > kMaxHeadElems) return FA_ERR_SHAPE;
     if (!aligned16(o) || !aligned16(dO) || !aligned16(delta)) return FA_ERR_ALIGN;
@@ -158,9 +154,9 @@ static fa_status_t bwd_common(const void* q, const void* k, const void* v, const
     if (!q || !k || !v || !dO || !lse || !delta) return FA_ERR_NULL;
     fa_status_t st = check_dtype(dtype);
     if (st != FA_OK) return st;
-    st = check_attn(B, Hq, Hkv, Lq, Lkv, D, scale, window, dtype);
+    st = check_attn(B, Hq, Hkv, Lq, Lkv, D, scale, window);
     if (st != FA_OK) return st;
-    st = check_dv(B, Hq, Hkv, Lq, Lkv, Dv, dtype);
+    st = check_dv(B, Hq, Hkv, Lq, Lkv, Dv);
     if (st != FA_OK) return st;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(lse) || !aligned16(delta))
         return FA_ERR_ALIGN;

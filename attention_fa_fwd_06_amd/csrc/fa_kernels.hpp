@@ -161,6 +161,21 @@ template <> struct MmaTr<float> {
     }
 };
 
+// float only: acc += X^T * pf with X read element by element from its natural
+// (row-major) LDS copy, for tiles whose transposed copy does not fit. p points
+// at row 16g + 4h of X and at the lane's column; pitch is the row pitch. The
+// rows taken follow the accumulator rows that make_pf packs into lo and hi.
+__device__ __forceinline__ void mma_rows_f32(f32x16& acc, const char* p, int pitch, const PF<float>& pf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(*reinterpret_cast<const float*>(p + i * pitch), pf.lo[i], acc, 0,
+                                                   0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(*reinterpret_cast<const float*>(p + (8 + i) * pitch), pf.hi[i],
+                                                   acc, 0, 0, 0);
+}
+
 // Four fp32 values -> four elements of T, stored at p (8 or 16 bytes).
 template <class T> __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
 template <> __device__ __forceinline__ void store4<__bf16>(__bf16* p, float a, float b, float c, float d) {
@@ -619,8 +634,15 @@ template <class T, int DMAX, int BKV, int RW, int DW> struct DqCfg {
     static constexpr int TSTR = BKV * (int)sizeof(T) + 16;
     static constexpr int KBYTES = BKV * KSTR;
     static constexpr int TBYTES = DMAX * TSTR;
-    static constexpr int STAGE = 2 * KBYTES + TBYTES;  // K, V natural + K transposed
-    static constexpr int RED = DW > 1 ? 2 * RW * DW * NKB * 16 * 64 * 4 : 0;
+    // Head dim 512 (float): no transposed K copy (the dQ product reads K
+    // element by element from the natural copy), and the S and dP partial
+    // sums take turns in one buffer, one extra barrier apart.
+    static constexpr bool TR = DMAX <= 256;
+    static_assert(TR || sizeof(T) == 4, "the natural-copy dQ product is float only");
+    static constexpr int STAGE = 2 * KBYTES + (TR ? TBYTES : 0);  // K, V natural (+ K transposed)
+    static constexpr int RED1 = DW > 1 ? RW * DW * NKB * 16 * 64 * 4 : 0;
+    static constexpr bool SEQ = !TR;
+    static constexpr int RED = (SEQ ? 1 : 2) * RED1;
     static constexpr bool DB = 2 * STAGE + RED <= kLdsBudget / 2 || (DMAX <= 128 && 2 * STAGE + RED <= kLdsBudget);
     static constexpr int LDS = (DB ? 2 : 1) * STAGE + RED;
     static_assert(LDS <= kLdsBudget, "dQ tile does not fit in LDS");
@@ -695,7 +717,8 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_kernel(BwdArgs a) {
         }
         if constexpr (DW > 1) {
             reduce_partials<DW, C::NKB>(s, red, rw * DW, dw, lane);
-            reduce_partials<DW, C::NKB>(dp, red + RW * DW * C::NKB * 16 * 64, rw * DW, dw, lane);
+            if constexpr (C::SEQ) __syncthreads();  // every wave has read the S sums
+            reduce_partials<DW, C::NKB>(dp, red + (C::SEQ ? 0 : RW * DW * C::NKB * 16 * 64), rw * DW, dw, lane);
         }
         const bool need = (t0 + BKV > a.Lkv) || (a.causal && t0 + BKV - 1 > i0) ||
                           (a.window && i_last - t0 >= a.window);
@@ -720,18 +743,27 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_kernel(BwdArgs a) {
         PF<T> pf[C::NPG];
 #pragma unroll
         for (int gg = 0; gg < C::NPG; ++gg) pf[gg] = make_pf<T>(s[gg >> 1], gg & 1);
+        if constexpr (C::TR) {
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-            const char* ka = ktl + (dw * C::DS + 32 * db + ln) * C::TSTR + 8 * h * (int)sizeof(T);
+            for (int db = 0; db < C::NDB; ++db) {
+                const char* ka = ktl + (dw * C::DS + 32 * db + ln) * C::TSTR + 8 * h * (int)sizeof(T);
 #pragma unroll
-            for (int gg = 0; gg < C::NPG; ++gg) MmaTr<T>::run(acc[db], ka + 16 * gg * (int)sizeof(T), pf[gg]);
+                for (int gg = 0; gg < C::NPG; ++gg) MmaTr<T>::run(acc[db], ka + 16 * gg * (int)sizeof(T), pf[gg]);
+            }
+        } else {
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db) {
+                const char* ka = kl + 4 * h * C::KSTR + (dw * C::DS + 32 * db + ln) * (int)sizeof(T);
+#pragma unroll
+                for (int gg = 0; gg < C::NPG; ++gg) mma_rows_f32(acc[db], ka + 16 * gg * C::KSTR, C::KSTR, pf[gg]);
+            }
         }
     };
 
     auto stage_store = [&](char* st) {
         kt.store_nat(st, C::KSTR, tid);
         vt.store(st + C::KBYTES, C::KSTR, tid);
-        kt.store_tr(st + 2 * C::KBYTES, C::TSTR, tid);
+        if constexpr (C::TR) kt.store_tr(st + 2 * C::KBYTES, C::TSTR, tid);
     };
 
     if constexpr (C::DB) {
@@ -798,13 +830,21 @@ template <class T, int DMAX, int BQ, int KW, int DW> struct DkvCfg {
     static constexpr int TSTR = BQ * (int)sizeof(T) + 16;
     static constexpr int QBYTES = BQ * QSTR;
     static constexpr int TBYTES = DMAX * TSTR;
-    static constexpr int STAGE = 2 * QBYTES + 2 * TBYTES + 2 * BQ * 4;  // Q, dO, Q^T, dO^T, lse2, delta
-    static constexpr int RED = DW > 1 ? 2 * KW * DW * NRB * 16 * 64 * 4 : 0;
+    // Head dim 512 (float): no transposed Q/dO copies (the dV and dK products
+    // read them element by element from the natural copies), and the S and
+    // dP partial sums take turns in one buffer, one extra barrier apart.
+    static constexpr bool TR = DMAX <= 256;
+    static_assert(TR || sizeof(T) == 4, "the natural-copy dK/dV products are float only");
+    static constexpr int TOFF = 2 * QBYTES + (TR ? 2 * TBYTES : 0);  // lse2 and delta of the tile's rows
+    static constexpr int STAGE = TOFF + 2 * BQ * 4;                   // Q, dO (+ Q^T, dO^T), lse2, delta
+    static constexpr int RED1 = DW > 1 ? KW * DW * NRB * 16 * 64 * 4 : 0;
+    static constexpr bool SEQ = !TR;
+    static constexpr int RED = (SEQ ? 1 : 2) * RED1;
     static constexpr bool DB = 2 * STAGE + RED <= kLdsBudget;
     // When even one stage plus the partial-sum buffer overflows LDS, the
     // partial sums reuse the natural Q/dO copies, which are no longer read
     // once the partial score products are done (one extra barrier).
-    static constexpr bool ALIAS = !DB && STAGE + RED > kLdsBudget;
+    static constexpr bool ALIAS = TR && !DB && STAGE + RED > kLdsBudget;
     static_assert(!ALIAS || RED <= 2 * QBYTES, "partial sums must fit over the Q/dO copies");
     static constexpr int LDS = ALIAS ? STAGE : (DB ? 2 : 1) * STAGE + RED;
     static_assert(LDS <= kLdsBudget, "dK/dV tile does not fit in LDS");
@@ -875,9 +915,11 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_kernel(BwdArgs a) {
     auto store = [&](char* st) {
         qtile.store_nat(st, C::QSTR, tid);
         dtile.store_nat(st + C::QBYTES, C::QSTR, tid);
-        qtile.store_tr(st + 2 * C::QBYTES, C::TSTR, tid);
-        dtile.store_tr(st + 2 * C::QBYTES + C::TBYTES, C::TSTR, tid);
-        float* lf = reinterpret_cast<float*>(st + 2 * C::QBYTES + 2 * C::TBYTES);
+        if constexpr (C::TR) {
+            qtile.store_tr(st + 2 * C::QBYTES, C::TSTR, tid);
+            dtile.store_tr(st + 2 * C::QBYTES + C::TBYTES, C::TSTR, tid);
+        }
+        float* lf = reinterpret_cast<float*>(st + C::TOFF);
         if (tid < BQ) {
             lf[tid] = lse_r;
             lf[BQ + tid] = dl_r;
@@ -888,7 +930,7 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_kernel(BwdArgs a) {
         const char* dol = st + C::QBYTES;
         const char* qtl = st + 2 * C::QBYTES;
         const char* dotl = st + 2 * C::QBYTES + C::TBYTES;
-        const float* lf = reinterpret_cast<const float*>(st + 2 * C::QBYTES + 2 * C::TBYTES);
+        const float* lf = reinterpret_cast<const float*>(st + C::TOFF);
         const int q0 = (qt_lo + it % nqt) * BQ;
 
         f32x16 s[C::NRB], dp[C::NRB];
@@ -906,7 +948,8 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_kernel(BwdArgs a) {
         if constexpr (DW > 1) {
             if constexpr (C::ALIAS) __syncthreads();  // every wave is done with the natural copies
             reduce_partials<DW, C::NRB>(s, red, kw * DW, dw, lane);
-            reduce_partials<DW, C::NRB>(dp, red + KW * DW * C::NRB * 16 * 64, kw * DW, dw, lane);
+            if constexpr (C::SEQ) __syncthreads();  // every wave has read the S sums
+            reduce_partials<DW, C::NRB>(dp, red + (C::SEQ ? 0 : KW * DW * C::NRB * 16 * 64), kw * DW, dw, lane);
         }
         const bool need = (q0 + BQ > a.Lq) || (a.causal && j0 + C::BKV - 1 > q0) ||
                           (a.window && min(q0 + BQ, a.Lq) - 1 - j0 >= a.window);
@@ -942,13 +985,25 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_kernel(BwdArgs a) {
             pf[gg] = make_pf<T>(s[gg >> 1], gg & 1);
             sf[gg] = make_pf<T>(dp[gg >> 1], gg & 1);
         }
+        if constexpr (C::TR) {
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-            const int off = (dw * C::DS + 32 * db + ln) * C::TSTR + 8 * h * (int)sizeof(T);
+            for (int db = 0; db < C::NDB; ++db) {
+                const int off = (dw * C::DS + 32 * db + ln) * C::TSTR + 8 * h * (int)sizeof(T);
 #pragma unroll
-            for (int gg = 0; gg < C::NPG; ++gg) {
-                MmaTr<T>::run(dv[db], dotl + off + 16 * gg * (int)sizeof(T), pf[gg]);
-                MmaTr<T>::run(dk[db], qtl + off + 16 * gg * (int)sizeof(T), sf[gg]);
+                for (int gg = 0; gg < C::NPG; ++gg) {
+                    MmaTr<T>::run(dv[db], dotl + off + 16 * gg * (int)sizeof(T), pf[gg]);
+                    MmaTr<T>::run(dk[db], qtl + off + 16 * gg * (int)sizeof(T), sf[gg]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db) {
+                const int off = 4 * h * C::QSTR + (dw * C::DS + 32 * db + ln) * (int)sizeof(T);
+#pragma unroll
+                for (int gg = 0; gg < C::NPG; ++gg) {
+                    mma_rows_f32(dv[db], dol + off + 16 * gg * C::QSTR, C::QSTR, pf[gg]);
+                    mma_rows_f32(dk[db], ql + off + 16 * gg * C::QSTR, C::QSTR, sf[gg]);
+                }
             }
         }
     };
@@ -1067,8 +1122,8 @@ inline int dmax_bucket(int D) {
 // <KV or Q tile, waves along rows or keys, waves along d, minimum waves per
 // SIMD>. float operands take twice the registers of 16-bit ones, so forward
 // tiles at head dim 96/128 take 32 keys and most tables run one wave per
-// SIMD; 256 splits d in two slices of 128. float inputs stop at head dim 256:
-// their staged Q, dO, Q^T and dO^T tiles at 512 exceed the 160 KB of LDS.
+// SIMD; 256 splits d in two slices of 128 and 512 in four (one 32-row or
+// 32-key block per workgroup, the backward kernels without transposed copies).
 template <class T> hipError_t launch_fwd_t(int dmax, const FwdArgs& a, hipStream_t s) {
     static_assert(sizeof(T) == 4, "float tables");
     switch (dmax) {
@@ -1077,6 +1132,7 @@ template <class T> hipError_t launch_fwd_t(int dmax, const FwdArgs& a, hipStream
         case 96: return launch_fwd_cfg<T, 96, 32, 4, 1, 1>(a, s);
         case 128: return launch_fwd_cfg<T, 128, 32, 4, 1, 1>(a, s);
         case 256: return launch_fwd_cfg<T, 256, 32, 2, 2, 1>(a, s);
+        case 512: return launch_fwd_cfg<T, 512, 32, 1, 4, 1>(a, s);
     }
     return hipErrorInvalidValue;
 }
@@ -1088,6 +1144,7 @@ template <class T> hipError_t launch_dq_t(int dmax, const BwdArgs& a, hipStream_
         case 96: return launch_dq_cfg<T, 96, 32, 4, 1, 1>(a, s);
         case 128: return launch_dq_cfg<T, 128, 64, 4, 1, 1>(a, s);
         case 256: return launch_dq_cfg<T, 256, 32, 2, 2, 1>(a, s);
+        case 512: return launch_dq_cfg<T, 512, 32, 1, 4, 1>(a, s);
     }
     return hipErrorInvalidValue;
 }
@@ -1099,6 +1156,7 @@ template <class T> hipError_t launch_dkv_t(int dmax, const BwdArgs& a, hipStream
         case 96: return launch_dkv_cfg<T, 96, 64, 4, 1, 1>(a, s);
         case 128: return launch_dkv_cfg<T, 128, 64, 4, 1, 1>(a, s);
         case 256: return launch_dkv_cfg<T, 256, 32, 1, 2, 1>(a, s);
+        case 512: return launch_dkv_cfg<T, 512, 32, 1, 4, 1>(a, s);
     }
     return hipErrorInvalidValue;
 }

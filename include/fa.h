@@ -55,7 +55,7 @@
  * FA_ERR_LAUNCH reports a failure of the HIP launch itself.
  *
  * Limits: 1 <= B, Hq, Hkv, Lq, Lkv; Hq % Hkv == 0; 32 <= D <= 512 and
- * D % 8 == 0 (D <= 256 for FA_F32); window >= 0; scale finite; every pointer 16-byte aligned;
+ * D % 8 == 0; window >= 0; scale finite; every pointer 16-byte aligned;
  * B*Hq*Lq*D and B*Hkv*Lkv*D below 2^31; Lq*D and Lkv*D at most 2^29;
  * Lq, Lkv below 2^24.
  */
@@ -76,7 +76,7 @@ typedef enum {
     FA_OK = 0,
     FA_ERR_NULL = -1,    /* a required pointer is NULL */
     FA_ERR_SHAPE = -2,   /* a size is < 1, too large, or Hq % Hkv != 0 */
-    FA_ERR_HEADDIM = -3, /* D outside [32, 512] ([32, 256] for FA_F32) or not a multiple of 8 */
+    FA_ERR_HEADDIM = -3, /* D outside [32, 512] or not a multiple of 8 */
     FA_ERR_DTYPE = -4,   /* dtype is not one of fa_dtype_t */
     FA_ERR_ALIGN = -5,   /* a pointer is not 16-byte aligned */
     FA_ERR_ARG = -6,     /* negative window, non-finite scale, or a mask stride outside [0, 2^40] */
@@ -175,7 +175,7 @@ fa_status_t fa_bwd_dq_masked(const void* q, const void* k, const void* v, const 
  *   o, dO       : [B, Hq,  Lq,  Dv]     v, dv : [B, Hkv, Lkv, Dv]
  *   lse, delta  : [B, Hq,  Lq]
  * fa_bwd_preprocess is called with its D set to Dv. Dv follows the rules of
- * D (a multiple of 8 in [32, 512], at most 256 for FA_F32, the same size
+ * D (a multiple of 8 in [32, 512], the same size
  * limits for the tensors that carry it); both head dims are served by the
  * tile shape of the larger one (the columns past each tensor's own head dim
  * are zero in the tiles and never stored). mask == NULL means no mask (the

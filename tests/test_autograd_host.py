@@ -38,10 +38,10 @@ def _g(*shape, dtype=torch.bfloat16):
     (((1, 4, 8, 36), (1, 2, 8, 36), (1, 2, 8, 36)), torch.bfloat16, 0, "head dim 36"),
     (((1, 4, 8, 520), (1, 2, 8, 520), (1, 2, 8, 520)), torch.float16, 0, "head dim 520"),
     (((1, 4, 8, 24), (1, 2, 8, 24), (1, 2, 8, 24)), torch.float16, 0, "head dim 24"),
-    (((1, 4, 8, 264), (1, 2, 8, 264), (1, 2, 8, 264)), torch.float32, 0, "up to 256"),
+    (((1, 4, 8, 520), (1, 2, 8, 520), (1, 2, 8, 520)), torch.float32, 0, "head dim 520"),
     (((1, 4, 8, 64), (1, 2, 8, 64), (1, 2, 9, 64)), torch.bfloat16, 0, "differs from k"),
     (((1, 4, 8, 64), (1, 2, 8, 64), (1, 2, 8, 44)), torch.bfloat16, 0, "value head dim 44"),
-    (((1, 4, 8, 64), (1, 2, 8, 64), (1, 2, 8, 264)), torch.float32, 0, "value head dim up to 256"),
+    (((1, 4, 8, 64), (1, 2, 8, 64), (1, 2, 8, 520)), torch.float32, 0, "value head dim 520"),
     (((2, 4, 8, 64), (1, 2, 8, 64), (1, 2, 8, 64)), torch.bfloat16, 0, "disagree"),
     (((1, 4, 8, 64), (1, 2, 8, 64), (1, 2, 8, 64)), torch.bfloat16, -1, "window"),
     (((1, 4, 8, 64), (1, 2, 8, 64), (1, 2, 8, 64)), torch.float64, 0, "float64"),
@@ -58,3 +58,6 @@ def test_supported_shapes_pass_the_router():
     assert unsupported_reason(_g(1, 2, 10, 64), _g(1, 1, 12, 64), _g(1, 1, 12, 256)) is None
     q, k, v = (_g(1, 1, 8, 256, dtype=torch.float32) for _ in range(3))
     assert unsupported_reason(q, k, v) is None
+    q, k, v = (_g(1, 1, 8, 512, dtype=torch.float32) for _ in range(3))
+    assert unsupported_reason(q, k, v) is None
+    assert unsupported_reason(q, k, _g(1, 1, 8, 264, dtype=torch.float32)) is None

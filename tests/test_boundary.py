@@ -108,8 +108,7 @@ def test_dq_null_pointers(lib, which):
         (dict(D=24), HEADDIM),
         (dict(D=36), HEADDIM),
         (dict(D=520), HEADDIM),
-        (dict(D=264, dtype=fa.FA_F32), HEADDIM),
-        (dict(D=512, dtype=fa.FA_F32), HEADDIM),
+        (dict(D=520, dtype=fa.FA_F32), HEADDIM),
         (dict(dtype=3), DTYPE),
         (dict(dtype=-1), DTYPE),
         (dict(window=-1), ARG),
@@ -261,9 +260,10 @@ def test_extended_calls_null_and_dtype(lib):
     assert lib.fa_fwd_ex(d, P, P, None, P, P, fa.FA_BF16, None) == NULL
     assert lib.fa_bwd_dkv_ex(d, P, P, P, P, P, P, P, None, fa.FA_BF16, None) == NULL
     assert lib.fa_bwd_dq_ex(d, P, P, P, P, P, P, P, 4, None) == DTYPE
-    d32 = ctypes.byref(_desc(Dv=264))
-    assert lib.fa_fwd_ex(d32, P, P, P, P, P, fa.FA_F32, None) == HEADDIM
-    assert lib.fa_fwd_ex(d32, P + 4, P, P, P, P, fa.FA_F16, None) == ALIGN  # Dv = 264 is fine for 16-bit types
+    assert lib.fa_fwd_ex(ctypes.byref(_desc(Dv=520)), P, P, P, P, P, fa.FA_F32, None) == HEADDIM
+    d264 = ctypes.byref(_desc(Dv=264))
+    for dt in (fa.FA_F32, fa.FA_F16):  # Dv = 264 passes the head-dim check for every dtype
+        assert lib.fa_fwd_ex(d264, P + 4, P, P, P, P, dt, None) == ALIGN
 
 
 def test_descriptor_layout_matches_the_header():

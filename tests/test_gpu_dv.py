@@ -23,6 +23,8 @@ CASES = [
     (1, 2, 1, 100, 100, 128, 512, "f16", True, 0, False),
     (1, 2, 2, 64, 64, 160, 72, "f32", False, 0, False),
     (1, 4, 4, 120, 120, 64, 192, "bf16", False, 0, True),
+    (1, 2, 1, 80, 80, 512, 64, "f32", True, 0, False),
+    (1, 2, 2, 60, 75, 96, 320, "f32", False, 0, True),
 ]
 
 

@@ -44,6 +44,7 @@ CASES = [
     (1, 2, 2, 64, 96, 256, "f32", False, 0, "LK", (3,)),
     (2, 8, 2, 257, 257, 128, "f16", False, 33, "BHLK", ()),
     (1, 4, 4, 96, 96, 64, "bf16", False, 0, "LK", ()),
+    (1, 2, 1, 90, 90, 512, "f32", True, 30, "LK", (4,)),
 ]
 
 

@@ -158,6 +158,11 @@ SWEEP = [
     (1, 2, 2, 150, 260, 248, "f16", True, 40),
     (1, 8, 2, 96, 96, 256, "f16", True, 0),
     (2, 2, 1, 70, 45, 136, "bf16", False, 0),
+    # float in the 512 bucket (d in four slices, no transposed copies in the backward)
+    (1, 2, 1, 100, 100, 512, "f32", True, 0),
+    (1, 4, 2, 70, 90, 264, "f32", False, 0),
+    (1, 2, 2, 130, 130, 512, "f32", True, 50),
+    (2, 2, 1, 33, 20, 392, "f32", True, 0),
 ]
 
 
