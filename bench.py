@@ -239,8 +239,11 @@ def run(w, steps, warmup, with_cpu):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    # The chip's clocks take some 50-100 ms of back-to-back steps to settle
+    # (a 2048-token step runs 0.89 ms over its first 25 steps, 0.67 ms from
+    # about step 75 on), so the default warm-up covers well over that.
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", type=int, default=2, help="index into synth.WORKLOADS (default: the 2048-token GQA)")
     ap.add_argument("--also", type=str, default="0,1,3,5", help="comma list of extra workload indices reported inline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
