@@ -20,6 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 PROBE = os.path.join(PKG, "mfma_ceiling")
+LDS_PROBE = os.path.join(PKG, "lds_ceiling")
 ARCH = "gfx950"
 
 SOURCES = ["fa_api.cpp", "fa_kernels_f32.hip", "fa_kernels_f16.hip", "fa_kernels_bf16.hip"]
@@ -77,11 +78,12 @@ def build(verbose: bool = False, resource_usage: bool = False, defines=(), out: 
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, out)
     if out == LIB:
-        # measurement helper: the sustained MFMA rate and clock of this GPU
-        cmd = [_hipcc(), *COMMON, os.path.join(CSRC, "mfma_ceiling.hip"), "-o", PROBE]
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        # measurement helpers: the sustained MFMA rate and LDS read rate of this GPU
+        for src, exe in (("mfma_ceiling.hip", PROBE), ("lds_ceiling.hip", LDS_PROBE)):
+            cmd = [_hipcc(), *COMMON, os.path.join(CSRC, src), "-o", exe]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     if verbose or resource_usage:
         for log in logs:
             lines = [ln for ln in log.splitlines() if "packed-fp32-ops" not in ln]
