@@ -997,6 +997,13 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_lds_kernel(BwdArgs a
 // last one down with heads innermost, so the workgroups of a group stream the
 // same Q/dO tiles at about the same time through that XCD's L2.
 // ===========================================================================
+// dV wave of the paired dK/dV kernel (head dim not split): 1 runs it pipelined
+// across query tiles (scores of tile t+1 before the dV update of tile t, with
+// that tile's exponentials between the update's MFMAs), 0 in the plain order.
+#ifndef FA2_DKV_VPIPE
+#define FA2_DKV_VPIPE 1
+#endif
+
 template <class T, int DMAX, int BQ, int KW, int DW> struct DkvPipeCfg {
     static constexpr int NS = 3;  // tile t (computing), t+1 (landed), t+2 (in flight)
     static constexpr int NW = 2 * KW * DW, NT = 64 * NW, BKV = 32 * KW;
@@ -1131,6 +1138,220 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
 #pragma unroll
             for (int gi = 0; gi < C::NKG; ++gi) fr0[gi] = ld16(smem + aoff + to.natural(0, gi, cb));
 
+            if constexpr (V && DW == 1 && FA2_DKV_VPIPE) {
+                // dV wave, pipelined across query tiles. After the barrier of tile it
+                // come the score products of tile it+1 (visible since that barrier),
+                // then dV^T += dO^T P of tile it with the exponentials of tile it+1
+                // placed between its MFMAs, so that the exp phase of this wave runs
+                // under matrix-core work instead of after it. P of each tile is stored
+                // for the dK wave before the barrier that publishes it, as in the plain
+                // order, and read back from there for this wave's own dV update; the
+                // barrier sequence is the dK wave's.
+                constexpr int HG = C::NKG / 2;
+                f32x16 x[C::NRB];
+                u32x4 nx[C::NDB];  // dO^T fragments of the row group multiplied next
+                u32x4 px;          // P of that row group (operand of the dV update)
+                int qa = qt_hi, ha = 0;  // query tile and head (in the group) of the next scores
+
+                // S = Q K^T of the tile whose phase-A operand is at `sa`; row block 0's
+                // fragments are in fr0
+                auto scores = [&](const char* sa) {
+                    u32x4 fr1[C::NKG];
+                    if constexpr (C::NRB == 2) {
+#pragma unroll
+                        for (int gi = 0; gi < HG; ++gi) fr1[gi] = ld16(sa + to.natural(32, gi, cb));
+                    }
+                    sched_fence();
+                    x[0] = zero16();
+#pragma unroll
+                    for (int gi = 0; gi < C::NKG; ++gi) Mma<T>::nat(x[0], fr0[gi], bf[gi]);
+                    sched_fence();
+                    if constexpr (C::NRB == 2) {
+#pragma unroll
+                        for (int gi = HG; gi < C::NKG; ++gi) fr1[gi] = ld16(sa + to.natural(32, gi, cb));
+                        sched_fence();
+                        x[1] = zero16();
+#pragma unroll
+                        for (int gi = 0; gi < C::NKG; ++gi) Mma<T>::nat(x[1], fr1[gi], bf[gi]);
+                    }
+                    sched_fence();
+                };
+                // lse of the rows of row group gg (accumulator half gg%2 of row block
+                // gg/2) of the tile in stage `sa`: rows 32(gg/2) + 8qd + 4h + i for
+                // qd = 2(gg%2), 2(gg%2)+1
+                auto rows = [&](const char* sa, int gg, f32x4 (&lg)[2]) {
+                    const float* rowv = reinterpret_cast<const float*>(sa + 2 * C::TILEB) + 4 * h;
+#pragma unroll
+                    for (int k = 0; k < 2; ++k)
+                        lg[k] = *reinterpret_cast<const f32x4*>(rowv + 32 * (gg >> 1) + 8 * (2 * (gg & 1) + k));
+                };
+                // P of row group gg as MFMA operand, from its scores and the rows' lse.
+                // Element r of row block rb is row q0 + 4h + rel with rel = 32 rb +
+                // 8(r/4) + r%4; the rows this lane's key may see form one run of rel,
+                // [run.lo, run.hi) (masked tiles only).
+                struct Run {
+                    int lo, hi;
+                };
+                auto row_run = [&](int q0) {
+                    const int base = q0 + 4 * h;
+                    Run u{a.causal ? key - base : INT_MIN, a.Lq - base};
+                    if (a.window) u.hi = min(u.hi, key + a.window - base);
+                    return u;
+                };
+                auto probs = [&](int gg, const f32x4 (&lg)[2], int q0, int hq, Run u, auto masked) {
+                    const int rb = gg >> 1, hf = gg & 1;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int r = 8 * hf + i, rel = 32 * rb + 8 * (r >> 2) + (r & 3);
+                        const float l = lg[i >> 2][i & 3];
+                        float e;
+                        if constexpr (MASK) {
+                            const float* mb = mask_slice(a.mask, a.msb, a.msh, b, hq);
+                            e = mask_l2(mb, q0 + 4 * h + rel, key, a.Lq, a.Lkv) - lse_l2_masked(l);
+                        } else {
+                            e = -l * kLog2e;
+                        }
+                        float p = fast_exp2(fmaf(x[rb][r], a.c, e));
+                        if constexpr (decltype(masked)::value) p = (rel >= u.lo && rel < u.hi) ? p : 0.f;
+                        x[rb][r] = p;
+                    }
+                    return make_pf<T>(x[rb], hf).v;
+                };
+                auto needs_mask = [&](int q0) {
+                    return (q0 + BQ > a.Lq) || (a.causal && j0 + C::BKV - 1 > q0) ||
+                           (a.window && min(q0 + BQ, a.Lq) - 1 - j0 >= a.window);
+                };
+                auto next_tile = [&]() {
+                    if (++ha == reps) {
+                        ha = 0;
+                        --qa;
+                    }
+                };
+                // dO^T fragments of row group gg of the tile whose dO is at `tb`
+                auto dot_frags = [&](const char* tb, int gg, u32x4 (&f)[C::NDB]) {
+#pragma unroll
+                    for (int db = 0; db < C::NDB; ++db)
+                        f[db] = rd_tr(tb + to.transposed(gg, db, cb, 0), tb + to.transposed(gg, db, cb, 1));
+                };
+
+                // first tile: scores, P stored for the dK wave, its first dO^T row group
+                if (n_it > 0) {
+                    const int q0 = qa * BQ, hq = g * reps + ha;
+                    scores(smem + aoff);
+                    const Run u = row_run(q0);
+                    auto first = [&](auto masked) {
+#pragma unroll
+                        for (int gg = 0; gg < C::NPG; ++gg) {
+                            f32x4 lg[2];
+                            rows(smem, gg, lg);
+                            st16(pbase + gg * 1024, probs(gg, lg, q0, hq, u, masked));
+                        }
+                    };
+                    if (needs_mask(q0)) first(std::true_type{});
+                    else first(std::false_type{});
+                    dot_frags(smem + toff, 0, nx);
+                    next_tile();
+                }
+                // tiles 0 .. n_it-2: the dV update of tile it with the scores and P of
+                // tile it+1 (one code path for every tile, so the accumulators stay in
+                // place; element masks are applied to the packed P afterwards)
+                int slot = 0;
+                for (int it = 0; it + 1 < n_it; ++it) {
+                    const int nslot = slot == C::NS - 1 ? 0 : slot + 1;
+                    const char* tb = smem + slot * C::STAGEB + toff;  // dO of tile it
+                    const char* sn = smem + nslot * C::STAGEB;        // tile it+1
+                    const char* pcur = pbase + (it & 1) * C::PBUF;    // P of tile it
+                    wait_vm<0>();   // this wave's share of tile it+1
+                    lds_barrier();  // P of tile it visible; tile it+1 visible; tile it-1 done
+                    if (it + 2 < n_it) issue();
+                    px = ld16(pcur);
+                    const int q0 = qa * BQ, hq = g * reps + ha;
+#pragma unroll
+                    for (int gi = 0; gi < C::NKG; ++gi) fr0[gi] = ld16(sn + aoff + to.natural(0, gi, cb));
+                    sched_fence();
+                    // row group 0 of tile it while row block 0 of tile it+1 arrives
+#pragma unroll
+                    for (int db = 0; db < C::NDB; ++db) Mma<T>::nat(acc[db], nx[db], px);
+                    sched_fence();
+                    dot_frags(tb, 1, nx);
+                    px = ld16(pcur + 1024);
+                    scores(sn + aoff);
+                    f32x4 lg[2][2];  // lse of row group k of tile it+1 in lg[k % 2]
+                    rows(sn, 0, lg[0]);
+                    u32x4 pn[C::NPG];  // P of tile it+1
+                    // row groups 1.. of tile it, each group's MFMAs with the
+                    // exponentials of one row group of tile it+1
+#pragma unroll
+                    for (int gg = 1; gg < C::NPG; ++gg) {
+                        u32x4 nn[C::NDB], pq;
+                        if (gg + 1 < C::NPG) {
+                            dot_frags(tb, gg + 1, nn);
+                            pq = ld16(pcur + (gg + 1) * 1024);
+                        } else {
+                            dot_frags(sn + toff, 0, nn);
+                        }
+                        rows(sn, gg, lg[gg & 1]);
+#pragma unroll
+                        for (int db = 0; db < C::NDB; ++db) Mma<T>::nat(acc[db], nx[db], px);
+                        pn[gg - 1] = probs(gg - 1, lg[(gg - 1) & 1], q0, hq, Run{}, std::false_type{});
+#pragma unroll
+                        for (int db = 0; db < C::NDB; ++db) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // three LDS reads
+                            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+                        }
+                        sched_fence();
+#pragma unroll
+                        for (int db = 0; db < C::NDB; ++db) nx[db] = nn[db];
+                        if (gg + 1 < C::NPG) px = pq;
+                    }
+                    pn[C::NPG - 1] = probs(C::NPG - 1, lg[(C::NPG - 1) & 1], q0, hq, Run{}, std::false_type{});
+                    if (needs_mask(q0)) {
+                        // zero the packed probabilities of rows this key may not see
+                        const Run u = row_run(q0);
+#pragma unroll
+                        for (int gg = 0; gg < C::NPG; ++gg)
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) {
+                                const int r = 8 * (gg & 1) + 2 * k;
+                                const int rel = 32 * (gg >> 1) + 8 * (r >> 2) + (r & 3);  // rel + 1 in the high half
+                                const uint32_t keep = (rel >= u.lo && rel < u.hi ? 0x0000ffffu : 0u) |
+                                                      (rel + 1 >= u.lo && rel + 1 < u.hi ? 0xffff0000u : 0u);
+                                pn[gg][k] &= keep;
+                            }
+                    }
+                    char* pb = pbase + ((it + 1) & 1) * C::PBUF;
+#pragma unroll
+                    for (int gg = 0; gg < C::NPG; ++gg) st16(pb + gg * 1024, pn[gg]);
+                    next_tile();
+                    slot = nslot;
+                }
+                if (n_it > 0) {
+                    // last tile: its dV update alone
+                    const char* tb = smem + slot * C::STAGEB + toff;
+                    const char* pcur = pbase + ((n_it - 1) & 1) * C::PBUF;
+                    wait_vm<0>();
+                    lds_barrier();
+                    px = ld16(pcur);
+#pragma unroll
+                    for (int gg = 0; gg < C::NPG; ++gg) {
+                        u32x4 nn[C::NDB], pq;
+                        if (gg + 1 < C::NPG) {
+                            dot_frags(tb, gg + 1, nn);
+                            pq = ld16(pcur + (gg + 1) * 1024);
+                        }
+                        sched_fence();
+#pragma unroll
+                        for (int db = 0; db < C::NDB; ++db) Mma<T>::nat(acc[db], nx[db], px);
+                        sched_fence();
+                        if (gg + 1 < C::NPG) {
+#pragma unroll
+                            for (int db = 0; db < C::NDB; ++db) nx[db] = nn[db];
+                            px = pq;
+                        }
+                    }
+                }
+            } else {
             int slot = 0, qt_cur = qt_hi, hq_cnt = 0;
             for (int it = 0; it < n_it; ++it) {
                 const char* st = smem + slot * C::STAGEB;
@@ -1299,6 +1520,7 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
                     hq_cnt = 0;
                     --qt_cur;
                 }
+            }
             }
 
             if (key < a.Lkv) {
