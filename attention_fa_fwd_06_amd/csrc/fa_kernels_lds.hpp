@@ -136,13 +136,24 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 
 // Issue priority around the MFMA chains of the forward and dQ kernels (two
 // workgroups share a CU there): the wave in its product phase goes first, the
-// other wave's softmax VALU fills the issue slots in between (measured: D = 256
-// forward about 5 % faster, D = 128 forward and dQ unchanged).
+// other wave's softmax VALU fills the issue slots in between. In the forward
+// (ASYM) the product-phase priority also depends on the parity of the wave's
+// slot on its SIMD (HW_ID bits 3:0), so that of two waves in their product
+// phase at once one goes first. Measured on the causal GQA workloads: forward
+// 5 % faster at D = 256 with the plain priority; the asymmetric form takes the
+// D = 128 forward from 0.1605 to 0.1566 ms (three same-box A/B rounds) and is
+// no better for dQ.
 #ifndef FA2_MFMA_PRIO
 #define FA2_MFMA_PRIO 1
 #endif
-__device__ __forceinline__ void prio_mfma() {
-    if constexpr (FA2_MFMA_PRIO) __builtin_amdgcn_s_setprio(1);
+template <bool ASYM = false> __device__ __forceinline__ void prio_mfma() {
+    if constexpr (FA2_MFMA_PRIO && ASYM) {
+        const unsigned slot = __builtin_amdgcn_s_getreg(4 | (0 << 6) | (3 << 11));
+        if (slot & 1) __builtin_amdgcn_s_setprio(2);
+        else __builtin_amdgcn_s_setprio(1);
+    } else if constexpr (FA2_MFMA_PRIO) {
+        __builtin_amdgcn_s_setprio(1);
+    }
 }
 __device__ __forceinline__ void prio_valu() {
     if constexpr (FA2_MFMA_PRIO) __builtin_amdgcn_s_setprio(0);
@@ -390,7 +401,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
                 };
                 u32x4 cur[FB];
                 load(0, cur);
-                prio_mfma();
+                prio_mfma<true>();
 #pragma unroll
                 for (int k = 0; k < NB; ++k) {
                     u32x4 nxt[FB];
@@ -487,7 +498,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
                 }
                 l_run += ls0 + ls1;
             }
-            prio_mfma();
+            prio_mfma<true>();
 #pragma unroll
             for (int db = 0; db < C::NDB; ++db) {
                 u32x4 vnxt[C::NPG];
