@@ -1196,37 +1196,45 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
                     for (int k = 0; k < 2; ++k)
                         lg[k] = *reinterpret_cast<const f32x4*>(rowv + 32 * (gg >> 1) + 8 * (2 * (gg & 1) + k));
                 };
-                // P of row group gg as MFMA operand, from its scores and the rows' lse.
-                // Element r of row block rb is row q0 + 4h + rel with rel = 32 rb +
-                // 8(r/4) + r%4; the rows this lane's key may see form one run of rel,
-                // [run.lo, run.hi) (masked tiles only).
-                struct Run {
-                    int lo, hi;
-                };
-                auto row_run = [&](int q0) {
-                    const int base = q0 + 4 * h;
-                    Run u{a.causal ? key - base : INT_MIN, a.Lq - base};
-                    if (a.window) u.hi = min(u.hi, key + a.window - base);
-                    return u;
-                };
-                auto probs = [&](int gg, const f32x4 (&lg)[2], int q0, int hq, Run u, auto masked) {
+                // P of row group gg as MFMA operand, from its scores and the rows' lse
+                // (element masks are applied to the packed values by mask_p)
+                auto probs = [&](int gg, const f32x4 (&lg)[2], int q0, int hq) {
                     const int rb = gg >> 1, hf = gg & 1;
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
-                        const int r = 8 * hf + i, rel = 32 * rb + 8 * (r >> 2) + (r & 3);
+                        const int r = 8 * hf + i;
                         const float l = lg[i >> 2][i & 3];
                         float e;
                         if constexpr (MASK) {
                             const float* mb = mask_slice(a.mask, a.msb, a.msh, b, hq);
-                            e = mask_l2(mb, q0 + 4 * h + rel, key, a.Lq, a.Lkv) - lse_l2_masked(l);
+                            e = mask_l2(mb, q0 + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3), key, a.Lq, a.Lkv) -
+                                lse_l2_masked(l);
                         } else {
                             e = -l * kLog2e;
                         }
-                        float p = fast_exp2(fmaf(x[rb][r], a.c, e));
-                        if constexpr (decltype(masked)::value) p = (rel >= u.lo && rel < u.hi) ? p : 0.f;
-                        x[rb][r] = p;
+                        x[rb][r] = fast_exp2(fmaf(x[rb][r], a.c, e));
                     }
                     return make_pf<T>(x[rb], hf).v;
+                };
+                // Zero the packed probabilities of the rows this lane's key may not see.
+                // Element r of row block rb is row q0 + 4h + rel with rel = 32 rb + 8(r/4)
+                // + r%4; the allowed rows of a key form one run [lo, hi) of rel. Each
+                // 32-bit word holds elements r (low half) and r+1 (high half, rel + 1).
+                auto mask_p = [&](u32x4 (&pn)[C::NPG], int q0) {
+                    const int base = q0 + 4 * h;
+                    const int lo = a.causal ? key - base : INT_MIN;
+                    int hi = a.Lq - base;
+                    if (a.window) hi = min(hi, key + a.window - base);
+#pragma unroll
+                    for (int gg = 0; gg < C::NPG; ++gg)
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const int r = 8 * (gg & 1) + 2 * k;
+                            const int rel = 32 * (gg >> 1) + 8 * (r >> 2) + (r & 3);
+                            const uint32_t keep = (rel >= lo && rel < hi ? 0x0000ffffu : 0u) |
+                                                  (rel + 1 >= lo && rel + 1 < hi ? 0xffff0000u : 0u);
+                            pn[gg][k] &= keep;
+                        }
                 };
                 auto needs_mask = [&](int q0) {
                     return (q0 + BQ > a.Lq) || (a.causal && j0 + C::BKV - 1 > q0) ||
@@ -1249,17 +1257,16 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
                 if (n_it > 0) {
                     const int q0 = qa * BQ, hq = g * reps + ha;
                     scores(smem + aoff);
-                    const Run u = row_run(q0);
-                    auto first = [&](auto masked) {
+                    u32x4 pn[C::NPG];
 #pragma unroll
-                        for (int gg = 0; gg < C::NPG; ++gg) {
-                            f32x4 lg[2];
-                            rows(smem, gg, lg);
-                            st16(pbase + gg * 1024, probs(gg, lg, q0, hq, u, masked));
-                        }
-                    };
-                    if (needs_mask(q0)) first(std::true_type{});
-                    else first(std::false_type{});
+                    for (int gg = 0; gg < C::NPG; ++gg) {
+                        f32x4 lg[2];
+                        rows(smem, gg, lg);
+                        pn[gg] = probs(gg, lg, q0, hq);
+                    }
+                    if (needs_mask(q0)) mask_p(pn, q0);
+#pragma unroll
+                    for (int gg = 0; gg < C::NPG; ++gg) st16(pbase + gg * 1024, pn[gg]);
                     dot_frags(smem + toff, 0, nx);
                     next_tile();
                 }
@@ -1304,7 +1311,7 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
                         rows(sn, gg, lg[gg & 1]);
 #pragma unroll
                         for (int db = 0; db < C::NDB; ++db) Mma<T>::nat(acc[db], nx[db], px);
-                        pn[gg - 1] = probs(gg - 1, lg[(gg - 1) & 1], q0, hq, Run{}, std::false_type{});
+                        pn[gg - 1] = probs(gg - 1, lg[(gg - 1) & 1], q0, hq);
 #pragma unroll
                         for (int db = 0; db < C::NDB; ++db) {
                             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -1316,21 +1323,8 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
                         for (int db = 0; db < C::NDB; ++db) nx[db] = nn[db];
                         if (gg + 1 < C::NPG) px = pq;
                     }
-                    pn[C::NPG - 1] = probs(C::NPG - 1, lg[(C::NPG - 1) & 1], q0, hq, Run{}, std::false_type{});
-                    if (needs_mask(q0)) {
-                        // zero the packed probabilities of rows this key may not see
-                        const Run u = row_run(q0);
-#pragma unroll
-                        for (int gg = 0; gg < C::NPG; ++gg)
-#pragma unroll
-                            for (int k = 0; k < 4; ++k) {
-                                const int r = 8 * (gg & 1) + 2 * k;
-                                const int rel = 32 * (gg >> 1) + 8 * (r >> 2) + (r & 3);  // rel + 1 in the high half
-                                const uint32_t keep = (rel >= u.lo && rel < u.hi ? 0x0000ffffu : 0u) |
-                                                      (rel + 1 >= u.lo && rel + 1 < u.hi ? 0xffff0000u : 0u);
-                                pn[gg][k] &= keep;
-                            }
-                    }
+                    pn[C::NPG - 1] = probs(C::NPG - 1, lg[(C::NPG - 1) & 1], q0, hq);
+                    if (needs_mask(q0)) mask_p(pn, q0);
                     char* pb = pbase + ((it + 1) & 1) * C::PBUF;
 #pragma unroll
                     for (int gg = 0; gg < C::NPG; ++gg) st16(pb + gg * 1024, pn[gg]);
