@@ -1641,7 +1641,8 @@ inline int dmax16(int D) { return D <= 64 ? 64 : D <= 128 ? 128 : D <= 256 ? 256
 #endif
 
 // dK/dV on wave pairs: <query tile, key blocks of 32, waves splitting d, min waves per SIMD,
-// dV-wave priority>.
+// dV-wave priority>. At D = 256 (one wave per SIMD) the raised priority measured
+// 0.3375 against 0.3351 ms without it on the windowed 8192-token workload.
 #ifndef FA2_DKVS_64
 #define FA2_DKVS_64 64, 4, 1, 2, 1
 #endif
@@ -1649,7 +1650,7 @@ inline int dmax16(int D) { return D <= 64 ? 64 : D <= 128 ? 128 : D <= 256 ? 256
 #define FA2_DKVS_128 64, 4, 1, 2, 1
 #endif
 #ifndef FA2_DKVS_256
-#define FA2_DKVS_256 32, 2, 1, 1, 1
+#define FA2_DKVS_256 32, 2, 1, 1, 0
 #endif
 
 }  // namespace lds
