@@ -17,10 +17,12 @@ caller-allocated tensors):
 Convenience wrappers that allocate their outputs:
     forward(q, k, v, scale=None, causal=False, window=0, mask=None) -> (o, lse)
     backward(q, k, v, o, lse, do, scale=None, causal=False, window=0, mask=None) -> (dq, dk, dv)
-A mask is a float32 GPU tensor whose last two dims are [Lq, Lkv] (contiguous
-rows); up to two leading dims broadcast against [B, Hq] the way torch aligns
-shapes (right-aligned, size 1 or the full size). It is added to the scaled
-scores (0 attends, -inf blocks).
+A mask is a float32 or bool GPU tensor whose last two dims are [Lq, Lkv]
+(contiguous rows); up to two leading dims broadcast against [B, Hq] the way
+torch aligns shapes (right-aligned, size 1 or the full size). A float32 mask
+is added to the scaled scores (0 attends, -inf blocks); a bool mask is True
+where the pair may attend (it runs through the extended calls, which read it
+as one byte per pair).
 """
 from __future__ import annotations
 
@@ -147,14 +149,15 @@ def _attn_shapes(q, k, v):
 
 
 def _mask_args(mask, B, Hq, Lq, Lkv, dev):
-    """(pointer, batch stride, head stride) of an additive float32 mask tensor
-    broadcast to [B, Hq, Lq, Lkv] (see include/fa.h, masked variants)."""
+    """(pointer, batch stride, head stride, is_bool) of an additive float32 or a
+    boolean mask tensor broadcast to [B, Hq, Lq, Lkv] (see include/fa.h, masked
+    variants and bool_mask of the extended calls); strides in elements."""
     import torch
 
     if not mask.is_cuda or mask.device != dev:
         raise ValueError(f"mask must be on {dev}")
-    if mask.dtype != torch.float32:
-        raise ValueError(f"mask must be float32, got {mask.dtype}")
+    if mask.dtype not in (torch.float32, torch.bool):
+        raise ValueError(f"mask must be float32 or bool, got {mask.dtype}")
     if mask.dim() < 2 or mask.dim() > 4 or tuple(mask.shape[-2:]) != (Lq, Lkv):
         raise ValueError(f"mask shape {tuple(mask.shape)} must end in [Lq, Lkv] = [{Lq}, {Lkv}] with at most 4 dims")
     if mask.stride(-1) != 1 or (Lq > 1 and mask.stride(-2) != Lkv):
@@ -166,7 +169,7 @@ def _mask_args(mask, B, Hq, Lq, Lkv, dev):
             raise ValueError(f"mask {name} dim is {size}; it must be 1 or {full}")
     msb = strides[0] if lead[0] > 1 else 0
     msh = strides[1] if lead[1] > 1 else 0
-    return mask.data_ptr(), int(msb), int(msh)
+    return mask.data_ptr(), int(msb), int(msh), mask.dtype == torch.bool
 
 
 class FaAttnDesc(ctypes.Structure):
@@ -175,13 +178,20 @@ class FaAttnDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int), ("Lq", ctypes.c_int),
                 ("Lkv", ctypes.c_int), ("D", ctypes.c_int), ("Dv", ctypes.c_int), ("scale", ctypes.c_float),
                 ("causal", ctypes.c_int), ("window", ctypes.c_int), ("mask", ctypes.c_void_p),
-                ("mask_stride_b", ctypes.c_longlong), ("mask_stride_h", ctypes.c_longlong)]
+                ("mask_stride_b", ctypes.c_longlong), ("mask_stride_h", ctypes.c_longlong),
+                ("bool_mask", ctypes.c_void_p)]
 
 
 def _desc(dims, scale, causal, window, margs):
     B, Hq, Hkv, Lq, Lkv, D, Dv = dims
-    ptr, msb, msh = margs if margs is not None else (None, 0, 0)
-    return FaAttnDesc(B, Hq, Hkv, Lq, Lkv, D, Dv, float(scale), int(bool(causal)), int(window), ptr, msb, msh)
+    ptr, msb, msh, is_bool = margs if margs is not None else (None, 0, 0, False)
+    return FaAttnDesc(B, Hq, Hkv, Lq, Lkv, D, Dv, float(scale), int(bool(causal)), int(window),
+                      None if is_bool else ptr, msb, msh, ptr if is_bool else None)
+
+
+def _extended(dims, margs):
+    """The extended calls serve a value head dim other than D and bool masks."""
+    return dims[6] != dims[5] or (margs is not None and margs[3])
 
 
 def fa_fwd(q, k, v, o, lse, scale, causal=False, window=0, mask=None):
@@ -198,7 +208,7 @@ def fa_fwd(q, k, v, o, lse, scale, causal=False, window=0, mask=None):
     ins = (_ptr(q, "q", dev, dt), _ptr(k, "k", dev, dt), _ptr(v, "v", dev, dt))
     outs = (_ptr(o, "o", dev, dt), _ptr(lse, "lse", dev, torch.float32))
     margs = None if mask is None else _mask_args(mask, B, Hq, Lq, Lkv, dev)
-    if Dv != D:
+    if _extended(dims, margs):
         desc = _desc(dims, scale, causal, window, margs)
         _check("fa_fwd_ex", lib.fa_fwd_ex(ctypes.byref(desc), *ins, *outs, _dtype_code(q), _stream(dev)))
         return
@@ -206,7 +216,7 @@ def fa_fwd(q, k, v, o, lse, scale, causal=False, window=0, mask=None):
     if mask is None:
         _check("fa_fwd", lib.fa_fwd(*ins, *outs, *rest))
     else:
-        _check("fa_fwd_masked", lib.fa_fwd_masked(*ins, *margs, *outs, *rest))
+        _check("fa_fwd_masked", lib.fa_fwd_masked(*ins, *margs[:3], *outs, *rest))
 
 
 def fa_bwd_preprocess(o, do, delta):
@@ -247,7 +257,7 @@ def fa_bwd_dkv(q, k, v, do, lse, delta, dk, dv, scale, causal=False, window=0, m
         raise ValueError("dk must match k and dv must match v")
     outs = (_ptr(dk, "dk", dev, dt), _ptr(dv, "dv", dev, dt))
     margs = None if mask is None else _mask_args(mask, B, Hq, Lq, Lkv, dev)
-    if Dv != D:
+    if _extended(dims, margs):
         desc = _desc(dims, scale, causal, window, margs)
         _check("fa_bwd_dkv_ex", lib.fa_bwd_dkv_ex(ctypes.byref(desc), *ptrs, *outs, _dtype_code(q), _stream(dev)))
         return
@@ -255,7 +265,7 @@ def fa_bwd_dkv(q, k, v, do, lse, delta, dk, dv, scale, causal=False, window=0, m
     if mask is None:
         _check("fa_bwd_dkv", lib.fa_bwd_dkv(*ptrs, *outs, *rest))
     else:
-        _check("fa_bwd_dkv_masked", lib.fa_bwd_dkv_masked(*ptrs, *margs, *outs, *rest))
+        _check("fa_bwd_dkv_masked", lib.fa_bwd_dkv_masked(*ptrs, *margs[:3], *outs, *rest))
 
 
 def fa_bwd_dq(q, k, v, do, lse, delta, dq, scale, causal=False, window=0, mask=None):
@@ -266,7 +276,7 @@ def fa_bwd_dq(q, k, v, do, lse, delta, dq, scale, causal=False, window=0, mask=N
     if tuple(dq.shape) != tuple(q.shape):
         raise ValueError("dq must match q")
     margs = None if mask is None else _mask_args(mask, B, Hq, Lq, Lkv, dev)
-    if Dv != D:
+    if _extended(dims, margs):
         desc = _desc(dims, scale, causal, window, margs)
         _check("fa_bwd_dq_ex", lib.fa_bwd_dq_ex(ctypes.byref(desc), *ptrs, _ptr(dq, "dq", dev, dt), _dtype_code(q),
                                                 _stream(dev)))
@@ -275,7 +285,7 @@ def fa_bwd_dq(q, k, v, do, lse, delta, dq, scale, causal=False, window=0, mask=N
     if mask is None:
         _check("fa_bwd_dq", lib.fa_bwd_dq(*ptrs, _ptr(dq, "dq", dev, dt), *rest))
     else:
-        _check("fa_bwd_dq_masked", lib.fa_bwd_dq_masked(*ptrs, *margs, _ptr(dq, "dq", dev, dt), *rest))
+        _check("fa_bwd_dq_masked", lib.fa_bwd_dq_masked(*ptrs, *margs[:3], _ptr(dq, "dq", dev, dt), *rest))
 
 
 def default_scale(D: int) -> float:

@@ -65,6 +65,19 @@ fa_status_t check_mask(const float* mask, long long msb, long long msh) {
 int mask_vec4(const float* mask, long long msb, long long msh, int Lkv) {
     return aligned16(mask) && msb % 4 == 0 && msh % 4 == 0 && Lkv % 4 == 0;
 }
+// Boolean mask of the extended calls: one byte per pair, any alignment, the
+// same stride range. Four consecutive keys are one 4-byte load when every row
+// starts 4-byte aligned.
+fa_status_t check_bool_mask(long long msb, long long msh) {
+    if (msb < 0 || msh < 0 || msb > kMaxMaskStride || msh > kMaxMaskStride) return FA_ERR_ARG;
+    return FA_OK;
+}
+int bool_mask_vec4(const unsigned char* m, long long msb, long long msh, int Lkv) {
+    return (reinterpret_cast<uintptr_t>(m) & 3u) == 0 && msb % 4 == 0 && msh % 4 == 0 && Lkv % 4 == 0;
+}
+int vec4(const float* mask, const unsigned char* bmask, long long msb, long long msh, int Lkv) {
+    return mask ? mask_vec4(mask, msb, msh, Lkv) : bmask ? bool_mask_vec4(bmask, msb, msh, Lkv) : 0;
+}
 
 // A window of Lq or more keys never masks anything (i - j <= Lq - 1 for every
 // pair), so it is the same as no window; folding it to 0 also keeps the
@@ -83,14 +96,14 @@ const char* fa_status_string(fa_status_t s) {
         case FA_ERR_HEADDIM: return "head dim must be a multiple of 8 in [32, 512]";
         case FA_ERR_DTYPE: return "unsupported dtype (FA_F32, FA_F16 or FA_BF16)";
         case FA_ERR_ALIGN: return "every pointer must be 16-byte aligned";
-        case FA_ERR_ARG: return "window must be >= 0, scale finite and mask strides in [0, 2^40]";
+        case FA_ERR_ARG: return "window must be >= 0, scale finite, mask strides in [0, 2^40] and at most one mask";
         case FA_ERR_LAUNCH: return "HIP kernel launch failed";
     }
     return "unknown status";
 }
 
 static fa_status_t fwd_impl(const void* q, const void* k, const void* v, const float* mask, long long msb,
-                            long long msh, void* o, float* lse, int B, int Hq, int Hkv, int Lq, int Lkv, int D,
+                            long long msh, const unsigned char* bmask, void* o, float* lse, int B, int Hq, int Hkv, int Lq, int Lkv, int D,
                             int Dv, float scale, int causal, int window, fa_dtype_t dtype, void* stream) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     fa_status_t st = check_dtype(dtype);
@@ -103,7 +116,7 @@ static fa_status_t fwd_impl(const void* q, const void* k, const void* v, const f
 
     fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Lq, Lkv, D,
                   (float)((double)scale * 1.4426950408889634), causal ? 1 : 0, effective_window(window, Lq),
-                  mask, msb, msh, mask ? mask_vec4(mask, msb, msh, Lkv) : 0, Dv};
+                  mask, msb, msh, vec4(mask, bmask, msb, msh, Lkv), Dv, bmask};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     switch (dtype) {
         case FA_F32: return from_hip(fa::launch_fwd_f32(a, s));
@@ -115,7 +128,7 @@ static fa_status_t fwd_impl(const void* q, const void* k, const void* v, const f
 
 fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                    int Lq, int Lkv, int D, float scale, int causal, int window, fa_dtype_t dtype, void* stream) {
-    return fwd_impl(q, k, v, nullptr, 0, 0, o, lse, B, Hq, Hkv, Lq, Lkv, D, D, scale, causal, window, dtype, stream);
+    return fwd_impl(q, k, v, nullptr, 0, 0, nullptr, o, lse, B, Hq, Hkv, Lq, Lkv, D, D, scale, causal, window, dtype, stream);
 }
 
 fa_status_t fa_fwd_masked(const void* q, const void* k, const void* v, const float* mask, long long mask_stride_b,
@@ -123,7 +136,7 @@ fa_status_t fa_fwd_masked(const void* q, const void* k, const void* v, const flo
                           int D, float scale, int causal, int window, fa_dtype_t dtype, void* stream) {
     fa_status_t st = check_mask(mask, mask_stride_b, mask_stride_h);
     if (st != FA_OK) return st;
-    return fwd_impl(q, k, v, mask, mask_stride_b, mask_stride_h, o, lse, B, Hq, Hkv, Lq, Lkv, D, D, scale, causal,
+    return fwd_impl(q, k, v, mask, mask_stride_b, mask_stride_h, nullptr, o, lse, B, Hq, Hkv, Lq, Lkv, D, D, scale, causal,
                     window, dtype, stream);
 }
 
@@ -164,7 +177,8 @@ static fa_status_t bwd_common(const void* q, const void* k, const void* v, const
 }
 
 static fa_status_t dkv_impl(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                            const float* delta, const float* mask, long long msb, long long msh, void* dk, void* dv,
+                            const float* delta, const float* mask, long long msb, long long msh,
+                            const unsigned char* bmask, void* dk, void* dv,
                             int B, int Hq, int Hkv, int Lq, int Lkv, int D, int Dv, float scale, int causal,
                             int window, fa_dtype_t dtype, void* stream) {
     if (!dk || !dv) return FA_ERR_NULL;
@@ -174,7 +188,7 @@ static fa_status_t dkv_impl(const void* q, const void* k, const void* v, const v
 
     fa::BwdArgs a{q, k, v, dO, lse, delta, nullptr, dk, dv, B, Hq, Hkv, Lq, Lkv, D,
                   (float)((double)scale * 1.4426950408889634), scale, causal ? 1 : 0,
-                  effective_window(window, Lq), mask, msb, msh, mask ? mask_vec4(mask, msb, msh, Lkv) : 0, Dv};
+                  effective_window(window, Lq), mask, msb, msh, vec4(mask, bmask, msb, msh, Lkv), Dv, bmask};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     switch (dtype) {
         case FA_F32: return from_hip(fa::launch_dkv_f32(a, s));
@@ -187,7 +201,7 @@ static fa_status_t dkv_impl(const void* q, const void* k, const void* v, const v
 fa_status_t fa_bwd_dkv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                        const float* delta, void* dk, void* dv, int B, int Hq, int Hkv, int Lq, int Lkv, int D,
                        float scale, int causal, int window, fa_dtype_t dtype, void* stream) {
-    return dkv_impl(q, k, v, dO, lse, delta, nullptr, 0, 0, dk, dv, B, Hq, Hkv, Lq, Lkv, D, D, scale, causal, window,
+    return dkv_impl(q, k, v, dO, lse, delta, nullptr, 0, 0, nullptr, dk, dv, B, Hq, Hkv, Lq, Lkv, D, D, scale, causal, window,
                     dtype, stream);
 }
 
@@ -197,12 +211,13 @@ fa_status_t fa_bwd_dkv_masked(const void* q, const void* k, const void* v, const
                               int D, float scale, int causal, int window, fa_dtype_t dtype, void* stream) {
     fa_status_t st = check_mask(mask, mask_stride_b, mask_stride_h);
     if (st != FA_OK) return st;
-    return dkv_impl(q, k, v, dO, lse, delta, mask, mask_stride_b, mask_stride_h, dk, dv, B, Hq, Hkv, Lq, Lkv, D, D,
+    return dkv_impl(q, k, v, dO, lse, delta, mask, mask_stride_b, mask_stride_h, nullptr, dk, dv, B, Hq, Hkv, Lq, Lkv, D, D,
                     scale, causal, window, dtype, stream);
 }
 
 static fa_status_t dq_impl(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                           const float* delta, const float* mask, long long msb, long long msh, void* dq, int B,
+                           const float* delta, const float* mask, long long msb, long long msh,
+                           const unsigned char* bmask, void* dq, int B,
                            int Hq, int Hkv, int Lq, int Lkv, int D, int Dv, float scale, int causal, int window,
                            fa_dtype_t dtype, void* stream) {
     if (!dq) return FA_ERR_NULL;
@@ -212,7 +227,7 @@ static fa_status_t dq_impl(const void* q, const void* k, const void* v, const vo
 
     fa::BwdArgs a{q, k, v, dO, lse, delta, dq, nullptr, nullptr, B, Hq, Hkv, Lq, Lkv, D,
                   (float)((double)scale * 1.4426950408889634), scale, causal ? 1 : 0,
-                  effective_window(window, Lq), mask, msb, msh, mask ? mask_vec4(mask, msb, msh, Lkv) : 0, Dv};
+                  effective_window(window, Lq), mask, msb, msh, vec4(mask, bmask, msb, msh, Lkv), Dv, bmask};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     switch (dtype) {
         case FA_F32: return from_hip(fa::launch_dq_f32(a, s));
@@ -225,7 +240,7 @@ static fa_status_t dq_impl(const void* q, const void* k, const void* v, const vo
 fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                       const float* delta, void* dq, int B, int Hq, int Hkv, int Lq, int Lkv, int D, float scale,
                       int causal, int window, fa_dtype_t dtype, void* stream) {
-    return dq_impl(q, k, v, dO, lse, delta, nullptr, 0, 0, dq, B, Hq, Hkv, Lq, Lkv, D, D, scale, causal, window, dtype,
+    return dq_impl(q, k, v, dO, lse, delta, nullptr, 0, 0, nullptr, dq, B, Hq, Hkv, Lq, Lkv, D, D, scale, causal, window, dtype,
                    stream);
 }
 
@@ -235,15 +250,22 @@ fa_status_t fa_bwd_dq_masked(const void* q, const void* k, const void* v, const 
                              int window, fa_dtype_t dtype, void* stream) {
     fa_status_t st = check_mask(mask, mask_stride_b, mask_stride_h);
     if (st != FA_OK) return st;
-    return dq_impl(q, k, v, dO, lse, delta, mask, mask_stride_b, mask_stride_h, dq, B, Hq, Hkv, Lq, Lkv, D, D, scale,
+    return dq_impl(q, k, v, dO, lse, delta, mask, mask_stride_b, mask_stride_h, nullptr, dq, B, Hq, Hkv, Lq, Lkv, D, D, scale,
                    causal, window, dtype, stream);
 }
 
+// The descriptor's layout is part of the ABI (the Python binding mirrors it).
+static_assert(sizeof(fa_attn_desc_t) == 72 && offsetof(fa_attn_desc_t, mask) == 40 &&
+                  offsetof(fa_attn_desc_t, bool_mask) == 64,
+              "fa_attn_desc_t layout");
+
 // Extended calls: one descriptor carries the sizes (with a value head dim),
-// the mask flags and the optional mask.
+// the mask flags and the optional mask (additive or boolean, not both).
 static fa_status_t check_desc(const fa_attn_desc_t* d) {
     if (!d) return FA_ERR_NULL;
+    if (d->mask && d->bool_mask) return FA_ERR_ARG;
     if (d->mask) return check_mask(d->mask, d->mask_stride_b, d->mask_stride_h);
+    if (d->bool_mask) return check_bool_mask(d->mask_stride_b, d->mask_stride_h);
     return FA_OK;
 }
 
@@ -251,7 +273,7 @@ fa_status_t fa_fwd_ex(const fa_attn_desc_t* d, const void* q, const void* k, con
                       fa_dtype_t dtype, void* stream) {
     fa_status_t st = check_desc(d);
     if (st != FA_OK) return st;
-    return fwd_impl(q, k, v, d->mask, d->mask_stride_b, d->mask_stride_h, o, lse, d->B, d->Hq, d->Hkv, d->Lq,
+    return fwd_impl(q, k, v, d->mask, d->mask_stride_b, d->mask_stride_h, d->bool_mask, o, lse, d->B, d->Hq, d->Hkv, d->Lq,
                     d->Lkv, d->D, d->Dv, d->scale, d->causal, d->window, dtype, stream);
 }
 
@@ -259,7 +281,7 @@ fa_status_t fa_bwd_dkv_ex(const fa_attn_desc_t* d, const void* q, const void* k,
                           const float* lse, const float* delta, void* dk, void* dv, fa_dtype_t dtype, void* stream) {
     fa_status_t st = check_desc(d);
     if (st != FA_OK) return st;
-    return dkv_impl(q, k, v, dO, lse, delta, d->mask, d->mask_stride_b, d->mask_stride_h, dk, dv, d->B, d->Hq,
+    return dkv_impl(q, k, v, dO, lse, delta, d->mask, d->mask_stride_b, d->mask_stride_h, d->bool_mask, dk, dv, d->B, d->Hq,
                     d->Hkv, d->Lq, d->Lkv, d->D, d->Dv, d->scale, d->causal, d->window, dtype, stream);
 }
 
@@ -267,7 +289,7 @@ fa_status_t fa_bwd_dq_ex(const fa_attn_desc_t* d, const void* q, const void* k, 
                          const float* lse, const float* delta, void* dq, fa_dtype_t dtype, void* stream) {
     fa_status_t st = check_desc(d);
     if (st != FA_OK) return st;
-    return dq_impl(q, k, v, dO, lse, delta, d->mask, d->mask_stride_b, d->mask_stride_h, dq, d->B, d->Hq, d->Hkv,
+    return dq_impl(q, k, v, dO, lse, delta, d->mask, d->mask_stride_b, d->mask_stride_h, d->bool_mask, dq, d->B, d->Hq, d->Hkv,
                    d->Lq, d->Lkv, d->D, d->Dv, d->scale, d->causal, d->window, dtype, stream);
 }
 

@@ -317,27 +317,49 @@ __device__ __forceinline__ bool mask_ok(int i, int j, int causal, int window) {
 }
 
 // ---------------------------------------------------------------------------
-// Additive mask of the masked entry points (ggmlR R/ag_flash_attn.R,
-// ag_flash_attention `mask`: 0 attends, -inf blocks; a finite value is added
-// to the scaled score). Values come back multiplied by log2(e), ready to be
-// added to c * S in the exp2 domain; positions past Lq or Lkv read as 0 (the
-// flags mask them anyway).
+// Mask of the masked entry points (ggmlR R/ag_flash_attn.R, ag_flash_attention
+// `mask`, and .ag_flash_mask). Additive float32 form: 0 attends, -inf blocks,
+// a finite value is added to the scaled score. Boolean form (a byte per pair):
+// nonzero where attention is allowed, read as 0, and zero read as -inf — the
+// rule by which the pages turn a logical mask into the additive one. Values
+// come back multiplied by log2(e), ready to be added to c * S in the exp2
+// domain; positions past Lq or Lkv read as 0 (the flags mask them anyway).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ const float* mask_slice(const float* m, long long msb, long long msh, int b, int h) {
-    return m + b * msb + h * msh;
+struct MaskRow {
+    const float* f;          // additive mask of one (batch, head), or
+    const unsigned char* u;  // boolean mask of one (batch, head)
+};
+template <class A> __device__ __forceinline__ MaskRow mask_slice(const A& a, int b, int h) {
+    const long long off = b * a.msb + h * a.msh;
+    return a.bmask ? MaskRow{nullptr, a.bmask + off} : MaskRow{a.mask + off, nullptr};
 }
-__device__ __forceinline__ float mask_l2(const float* mb, int i, int j, int Lq, int Lkv) {
-    return (i < Lq && j < Lkv) ? mb[(size_t)i * Lkv + j] * kLog2e : 0.f;
+__device__ __forceinline__ float bool_l2(unsigned v) { return v ? 0.f : -INFINITY; }
+__device__ __forceinline__ float mask_l2(MaskRow mb, int i, int j, int Lq, int Lkv) {
+    if (!(i < Lq && j < Lkv)) return 0.f;
+    const size_t idx = (size_t)i * Lkv + j;
+    return mb.u ? bool_l2(mb.u[idx]) : mb.f[idx] * kLog2e;
 }
-// keys j0 .. j0+3 of row i; one 16-byte load when the caller guarantees the
-// alignment (vec) and the four keys exist
-__device__ __forceinline__ f32x4 mask4_l2(const float* mb, int i, int j0, int Lq, int Lkv, int vec) {
+// keys j0 .. j0+3 of row i; one load (16 bytes float, 4 bytes boolean) when the
+// caller guarantees the alignment (vec) and the four keys exist
+__device__ __forceinline__ f32x4 mask4_l2(MaskRow mb, int i, int j0, int Lq, int Lkv, int vec) {
     f32x4 r;
+    const size_t idx = (size_t)i * Lkv + j0;
+    if (mb.u) {
+        if (vec && i < Lq && j0 + 3 < Lkv) {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(mb.u + idx);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = bool_l2((w >> (8 * e)) & 0xffu);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = (i < Lq && j0 + e < Lkv) ? bool_l2(mb.u[idx + e]) : 0.f;
+        }
+        return r;
+    }
     if (vec && i < Lq && j0 + 3 < Lkv) {
-        r = *reinterpret_cast<const f32x4*>(mb + (size_t)i * Lkv + j0);
+        r = *reinterpret_cast<const f32x4*>(mb.f + idx);
     } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = (i < Lq && j0 + e < Lkv) ? mb[(size_t)i * Lkv + j0 + e] : 0.f;
+        for (int e = 0; e < 4; ++e) r[e] = (i < Lq && j0 + e < Lkv) ? mb.f[idx + e] : 0.f;
     }
     return r * kLog2e;
 }
@@ -445,7 +467,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_kernel(FwdArgs a) {
         if constexpr (DW > 1) reduce_partials<DW, C::NKB>(s, red, rw * DW, dw, lane);
         if constexpr (MASK) {
             // masked entry points: c S + log2(e) mask, from here on in the exp2 domain
-            const float* mb = mask_slice(a.mask, a.msb, a.msh, b, hq);
+            const MaskRow mb = mask_slice(a, b, hq);
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
@@ -682,7 +704,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_kernel(BwdArgs a) {
     const size_t lrow = (size_t)(b * a.Hq + hq) * a.Lq + row;
     const float lse2 = row < a.Lq ? (MASK ? lse_l2_masked(a.lse[lrow]) : a.lse[lrow] * kLog2e) : 0.f;
     const float dl = row < a.Lq ? a.delta[lrow] : 0.f;
-    const float* mb = MASK ? mask_slice(a.mask, a.msb, a.msh, b, hq) : nullptr;
+    const MaskRow mb = MASK ? mask_slice(a, b, hq) : MaskRow{nullptr, nullptr};
 
     f32x16 acc[C::NDB];
 #pragma unroll
@@ -965,7 +987,7 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_kernel(BwdArgs a) {
                     const int r = 4 * qd + i;
                     float p;
                     if constexpr (MASK) {
-                        const float* mb = mask_slice(a.mask, a.msb, a.msh, b, g * reps + it / nqt);
+                        const MaskRow mb = mask_slice(a, b, g * reps + it / nqt);
                         const float l2 = l4[i] == -INFINITY ? INFINITY : l4[i];
                         p = fast_exp2(fmaf(s[rb][r], a.c, mask_l2(mb, q0 + rl + i, key, a.Lq, a.Lkv) - l2));
                     } else {
@@ -1063,7 +1085,7 @@ template <class K> inline hipError_t set_lds(K kernel, int bytes) {
 template <class T, int DMAX, int BKV, int RW, int DW, int OCC>
 hipError_t launch_fwd_cfg(const FwdArgs& a, hipStream_t s) {
     using C = FwdCfg<T, DMAX, BKV, RW, DW>;
-    auto kern = a.mask ? fa_fwd_kernel<T, DMAX, BKV, RW, DW, OCC, true> : fa_fwd_kernel<T, DMAX, BKV, RW, DW, OCC, false>;
+    auto kern = (a.mask || a.bmask) ? fa_fwd_kernel<T, DMAX, BKV, RW, DW, OCC, true> : fa_fwd_kernel<T, DMAX, BKV, RW, DW, OCC, false>;
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
     const long long nqt = (a.Lq + C::BQ - 1) / C::BQ;
@@ -1075,7 +1097,7 @@ hipError_t launch_fwd_cfg(const FwdArgs& a, hipStream_t s) {
 template <class T, int DMAX, int BKV, int RW, int DW, int OCC>
 hipError_t launch_dq_cfg(const BwdArgs& a, hipStream_t s) {
     using C = DqCfg<T, DMAX, BKV, RW, DW>;
-    auto kern = a.mask ? fa_dq_kernel<T, DMAX, BKV, RW, DW, OCC, true> : fa_dq_kernel<T, DMAX, BKV, RW, DW, OCC, false>;
+    auto kern = (a.mask || a.bmask) ? fa_dq_kernel<T, DMAX, BKV, RW, DW, OCC, true> : fa_dq_kernel<T, DMAX, BKV, RW, DW, OCC, false>;
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
     const long long nqt = (a.Lq + C::BQ - 1) / C::BQ;
@@ -1087,7 +1109,7 @@ hipError_t launch_dq_cfg(const BwdArgs& a, hipStream_t s) {
 template <class T, int DMAX, int BQ, int KW, int DW, int OCC>
 hipError_t launch_dkv_cfg(const BwdArgs& a, hipStream_t s) {
     using C = DkvCfg<T, DMAX, BQ, KW, DW>;
-    auto kern = a.mask ? fa_dkv_kernel<T, DMAX, BQ, KW, DW, OCC, true> : fa_dkv_kernel<T, DMAX, BQ, KW, DW, OCC, false>;
+    auto kern = (a.mask || a.bmask) ? fa_dkv_kernel<T, DMAX, BQ, KW, DW, OCC, true> : fa_dkv_kernel<T, DMAX, BQ, KW, DW, OCC, false>;
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
     const long long nkt = (a.Lkv + C::BKV - 1) / C::BKV;

@@ -422,7 +422,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
             if constexpr (DW > 1) reduce_partials<DW, C::NKB>(s, red, rw * DW, dw, lane);
             if constexpr (MASK) {
                 // masked entry points: c S + log2(e) mask, from here on in the exp2 domain
-                const float* mb = mask_slice(a.mask, a.msb, a.msh, b, hq);
+                const MaskRow mb = mask_slice(a, b, hq);
 #pragma unroll
                 for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
@@ -594,7 +594,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
     }
     const size_t lrow = (size_t)(b * a.Hq + hq) * a.Lq + row;
     const float lse2 = row < a.Lq ? (MASK ? lse_l2_masked(a.lse[lrow]) : a.lse[lrow] * kLog2e) : 0.f;
-    const float* mb = MASK ? mask_slice(a.mask, a.msb, a.msh, b, hq) : nullptr;
+    const MaskRow mb = MASK ? mask_slice(a, b, hq) : MaskRow{nullptr, nullptr};
     const float dl = row < a.Lq ? a.delta[lrow] : 0.f;
 
     f32x16 acc[C::NDB];
@@ -929,7 +929,7 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_lds_kernel(BwdArgs a
                     const int r = 4 * qd + i;
                     float p;
                     if constexpr (MASK) {
-                        const float* mb = mask_slice(a.mask, a.msb, a.msh, b, g * reps + it / nqt);
+                        const MaskRow mb = mask_slice(a, b, g * reps + it / nqt);
                         p = fast_exp2(fmaf(s[rb][r], a.c, mask_l2(mb, q0 + rl + i, key, a.Lq, a.Lkv) -
                                                               lse_l2_masked(l4[i])));
                     } else {
@@ -1206,7 +1206,7 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
                         const float l = lg[i >> 2][i & 3];
                         float e;
                         if constexpr (MASK) {
-                            const float* mb = mask_slice(a.mask, a.msb, a.msh, b, hq);
+                            const MaskRow mb = mask_slice(a, b, hq);
                             e = mask_l2(mb, q0 + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3), key, a.Lq, a.Lkv) -
                                 lse_l2_masked(l);
                         } else {
@@ -1434,7 +1434,7 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
                     if constexpr (MASK) {
                         // log2(e) (mask - lse) of each element; rows without any allowed key
                         // get -inf
-                        const float* mb = mask_slice(a.mask, a.msb, a.msh, b, g * reps + hq_cnt);
+                        const MaskRow mb = mask_slice(a, b, g * reps + hq_cnt);
 #pragma unroll
                         for (int rb = 0; rb < C::NRB; ++rb)
 #pragma unroll
@@ -1553,7 +1553,7 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
 template <class T, int DMAX, int BKV, int RW, int DW, int OCC, int NS>
 hipError_t launch_fwd2(const FwdArgs& a, hipStream_t s) {
     using C = Fwd2Cfg<T, DMAX, BKV, RW, DW, NS>;
-    auto kern = a.mask ? fa_fwd_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS, true>
+    auto kern = (a.mask || a.bmask) ? fa_fwd_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS, true>
                        : fa_fwd_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS, false>;
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
@@ -1564,9 +1564,9 @@ hipError_t launch_fwd2(const FwdArgs& a, hipStream_t s) {
 template <class T, int DMAX, int BKV, int RW, int DW, int OCC, int NS>
 hipError_t launch_dq2(const BwdArgs& a, hipStream_t s) {
     using C = Dq2Cfg<T, DMAX, BKV, RW, DW, NS>;
-    auto kern = a.Dv != a.D ? (a.mask ? fa_dq_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS, true, true>
+    auto kern = a.Dv != a.D ? ((a.mask || a.bmask) ? fa_dq_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS, true, true>
                                       : fa_dq_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS, false, true>)
-                            : (a.mask ? fa_dq_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS, true, false>
+                            : ((a.mask || a.bmask) ? fa_dq_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS, true, false>
                                       : fa_dq_lds_kernel<T, DMAX, BKV, RW, DW, OCC, NS, false, false>);
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
@@ -1577,7 +1577,7 @@ hipError_t launch_dq2(const BwdArgs& a, hipStream_t s) {
 template <class T, int DMAX, int BQ, int KW, int DW, int OCC, int NS>
 hipError_t launch_dkv2(const BwdArgs& a, hipStream_t s) {
     using C = Dkv2Cfg<T, DMAX, BQ, KW, DW, NS>;
-    auto kern = a.mask ? fa_dkv_lds_kernel<T, DMAX, BQ, KW, DW, OCC, NS, true>
+    auto kern = (a.mask || a.bmask) ? fa_dkv_lds_kernel<T, DMAX, BQ, KW, DW, OCC, NS, true>
                        : fa_dkv_lds_kernel<T, DMAX, BQ, KW, DW, OCC, NS, false>;
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
@@ -1593,7 +1593,7 @@ constexpr int kPairMinGrid = 256;
 template <class T, int DMAX, int BQ, int KW, int DW, int OCC, int PRIO>
 hipError_t launch_dkv_pipe(const BwdArgs& a, hipStream_t s) {
     using C = DkvPipeCfg<T, DMAX, BQ, KW, DW>;
-    auto kern = a.mask ? fa_dkv_pipe_kernel<T, DMAX, BQ, KW, DW, OCC, PRIO, true>
+    auto kern = (a.mask || a.bmask) ? fa_dkv_pipe_kernel<T, DMAX, BQ, KW, DW, OCC, PRIO, true>
                        : fa_dkv_pipe_kernel<T, DMAX, BQ, KW, DW, OCC, PRIO, false>;
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;

@@ -227,7 +227,7 @@ __global__ __launch_bounds__(64 * KW, 1) void fa_fwd_short_kernel(FwdArgs a, Sho
         s += s1;
         if constexpr (MASK) {
             // masked entry points: c S + log2(e) mask, from here on in the exp2 domain
-            const float* mb = mask_slice(a.mask, a.msb, a.msh, R.b, hq);
+            const MaskRow mb = mask_slice(a, R.b, hq);
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
                 const f32x4 m4 = mask4_l2(mb, i, j0 + 8 * qd + 4 * h, a.Lq, a.Lkv, a.mvec);
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(64 * KW, 1) void fa_dq_short_kernel(BwdArgs a, Shor
     const size_t lrow = R.R0 + R.p;
     const float lse2 = R.valid ? (MASK ? lse_l2_masked(a.lse[lrow]) : a.lse[lrow] * kLog2e) : 0.f;
     const float dl = R.valid ? a.delta[lrow] : 0.f;
-    const float* mb = MASK ? mask_slice(a.mask, a.msb, a.msh, R.b, hq) : nullptr;
+    const MaskRow mb = MASK ? mask_slice(a, R.b, hq) : MaskRow{nullptr, nullptr};
 
     f32x16 acc[C::NDB];
 #pragma unroll
@@ -613,7 +613,7 @@ __global__ __launch_bounds__(64 * KW, OCC) void fa_dkv_short_kernel(BwdArgs a) {
                 float pv;
                 if constexpr (MASK) {
                     const int pr = min(prow, P - 1);
-                    const float* mb = mask_slice(a.mask, a.msb, a.msh, b, g * reps + pr / a.Lq);
+                    const MaskRow mb = mask_slice(a, b, g * reps + pr / a.Lq);
                     pv = fast_exp2(fmaf(s[r], a.c, mask_l2(mb, pr % a.Lq, key, a.Lq, a.Lkv) - lse_l2_masked(l4[e])));
                 } else {
                     pv = fast_exp2(fmaf(s[r], a.c, -l4[e] * kLog2e));
@@ -700,7 +700,7 @@ inline ShortLaunch short_launch(int Hq, int Hkv, int Lq, int Lkv, long long grou
 template <class T, int DMAX, int KW, int NS>
 hipError_t launch_fwd_short(const FwdArgs& a, hipStream_t s) {
     using C = ShortCfg<DMAX, KW, NS>;
-    auto kern = a.mask ? fa_fwd_short_kernel<T, DMAX, KW, NS, true> : fa_fwd_short_kernel<T, DMAX, KW, NS, false>;
+    auto kern = (a.mask || a.bmask) ? fa_fwd_short_kernel<T, DMAX, KW, NS, true> : fa_fwd_short_kernel<T, DMAX, KW, NS, false>;
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
     int lds;
@@ -712,9 +712,9 @@ hipError_t launch_fwd_short(const FwdArgs& a, hipStream_t s) {
 template <class T, int DMAX, int KW, int NS>
 hipError_t launch_dq_short(const BwdArgs& a, hipStream_t s) {
     using C = ShortCfg<DMAX, KW, NS>;
-    auto kern = a.Dv != a.D ? (a.mask ? fa_dq_short_kernel<T, DMAX, KW, NS, true, true>
+    auto kern = a.Dv != a.D ? ((a.mask || a.bmask) ? fa_dq_short_kernel<T, DMAX, KW, NS, true, true>
                                       : fa_dq_short_kernel<T, DMAX, KW, NS, false, true>)
-                            : (a.mask ? fa_dq_short_kernel<T, DMAX, KW, NS, true, false>
+                            : ((a.mask || a.bmask) ? fa_dq_short_kernel<T, DMAX, KW, NS, true, false>
                                       : fa_dq_short_kernel<T, DMAX, KW, NS, false, false>);
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
@@ -727,7 +727,7 @@ hipError_t launch_dq_short(const BwdArgs& a, hipStream_t s) {
 template <class T, int DMAX, int KW, int NS, int OCC>
 hipError_t launch_dkv_short(const BwdArgs& a, hipStream_t s) {
     using C = ShortDkvCfg<DMAX, KW, NS>;
-    auto kern = a.mask ? fa_dkv_short_kernel<T, DMAX, KW, NS, OCC, true>
+    auto kern = (a.mask || a.bmask) ? fa_dkv_short_kernel<T, DMAX, KW, NS, OCC, true>
                        : fa_dkv_short_kernel<T, DMAX, KW, NS, OCC, false>;
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;

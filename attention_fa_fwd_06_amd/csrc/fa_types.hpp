@@ -21,8 +21,11 @@ struct FwdArgs {
     // (b, h, i, j) at mask[b * msb + h * msh + i * Lkv + j]
     const float* mask;
     long long msb, msh;
-    int mvec;     // rows of four keys may be read as one 16-byte load
+    int mvec;     // rows of four keys may be read with one load (16 bytes float, 4 bytes boolean)
     int Dv;       // value head dim (v, o): D unless the extended call sets another
+    // boolean mask (extended entry points only; nullptr otherwise, and never
+    // together with `mask`): same indexing, nonzero = the pair may attend
+    const unsigned char* bmask;
 };
 
 // Backward pre-pass: delta = rowsum(dO * O) over rows of length D.
@@ -54,6 +57,7 @@ struct BwdArgs {
     long long msb, msh;
     int mvec;
     int Dv;       // value head dim (v, dO, dV)
+    const unsigned char* bmask;  // as in FwdArgs
 };
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);

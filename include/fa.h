@@ -181,6 +181,17 @@ fa_status_t fa_bwd_dq_masked(const void* q, const void* k, const void* v, const 
  * are zero in the tiles and never stored). mask == NULL means no mask (the
  * strides are then ignored); otherwise it is read exactly as by the masked
  * calls. desc == NULL returns FA_ERR_NULL.
+ *
+ * bool_mask (ggmlR R/ag_flash_attn.R, .ag_flash_mask: a logical mask is the
+ * friendlier spelling, TRUE where attention is allowed, and stands for 0 where
+ * TRUE and -Inf where FALSE): one byte per (query, key) pair, indexed with the
+ * same strides (in bytes, since an element is one byte) and broadcasting as the
+ * additive mask; a nonzero byte lets the pair attend, a zero byte removes it.
+ * It behaves exactly as the additive mask holding 0 and -inf in those places,
+ * at a quarter of its size. Any alignment is accepted (four keys are read with
+ * one 4-byte load when the pointer is 4-byte aligned and Lkv and both strides
+ * are multiples of 4). mask and bool_mask may not both be set (FA_ERR_ARG);
+ * the strides must lie in [0, 2^40] (FA_ERR_ARG).
  */
 typedef struct {
     int B, Hq, Hkv, Lq, Lkv;
@@ -192,6 +203,7 @@ typedef struct {
     const float* mask;          /* optional additive mask (device pointer) */
     long long mask_stride_b;    /* element strides of the mask, 0 broadcasts */
     long long mask_stride_h;
+    const unsigned char* bool_mask; /* optional boolean mask (device pointer) */
 } fa_attn_desc_t;
 
 fa_status_t fa_fwd_ex(const fa_attn_desc_t* desc, const void* q, const void* k, const void* v,

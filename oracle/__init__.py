@@ -5,6 +5,7 @@ from .attention import (  # noqa: F401
     bwd_preprocess,
     forward,
     key_span,
+    logical_mask_bias,
     mask_matrix,
     rows_forward,
     sample_keys,

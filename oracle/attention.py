@@ -35,6 +35,9 @@ Sources (the pages this follows):
     it is the `bias` argument, indexed [.., query, key]; a finite value is
     added to the scaled score (the reading under which 0 leaves a score alone
     and -Inf removes it), and it carries no gradient.
+  * ggmlR R/ag_flash_attn.R, `.ag_flash_mask`: a logical mask is TRUE where
+    attention is allowed and stands for the numeric mask with 0 there and
+    -Inf elsewhere (`logical_mask_bias`).
 
 Readings where the pages are silent or disagree (each listed in the design notes):
   * a row whose every key is masked gets O = 0, LSE = -inf and contributes no
@@ -129,6 +132,14 @@ def key_span(rows, Lkv, causal, window):
     lo = max(0, int(rows.min()) - window + 1) if window else 0
     hi = min(Lkv - 1, int(rows.max())) if causal else Lkv - 1
     return np.arange(lo, hi + 1) if hi >= lo else np.arange(0)
+
+
+def logical_mask_bias(allowed_pairs) -> np.ndarray:
+    """The numeric mask a logical mask stands for (ggmlR R/ag_flash_attn.R,
+    `.ag_flash_mask`): 0 where the entry is TRUE (attention allowed), -Inf where
+    it is FALSE. Any shape; float64 of the same shape, usable as `bias`."""
+    m = np.asarray(allowed_pairs, dtype=bool)
+    return np.where(m, 0.0, -np.inf)
 
 
 def _bias(bias, B, Hq, Lq, Lkv):

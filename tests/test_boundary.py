@@ -229,7 +229,7 @@ def test_binding_mask_shape_checks(lib):
 
 def _desc(**kw):
     d = dict(B=1, Hq=4, Hkv=2, Lq=64, Lkv=64, D=64, Dv=128, scale=0.125, causal=1, window=0, mask=None,
-             mask_stride_b=0, mask_stride_h=0)
+             mask_stride_b=0, mask_stride_h=0, bool_mask=None)
     d.update(kw)
     return fa.FaAttnDesc(**d)
 
@@ -243,6 +243,10 @@ def _desc(**kw):
     (dict(window=-2), ARG),
     (dict(mask=P + 2), ALIGN),
     (dict(mask=P, mask_stride_h=-1), ARG),
+    (dict(mask=P, bool_mask=P), ARG),                  # at most one mask
+    (dict(bool_mask=P + 1, mask_stride_b=-1), ARG),
+    (dict(bool_mask=P + 1, mask_stride_h=(1 << 40) + 1), ARG),
+    (dict(bool_mask=P + 1, Dv=36), HEADDIM),            # a byte mask needs no alignment
     (dict(Lq=(1 << 21) + 8, Lkv=64, Dv=256), SHAPE),
 ])
 def test_extended_calls_check_the_descriptor(lib, kw, code):
@@ -267,6 +271,8 @@ def test_extended_calls_null_and_dtype(lib):
 
 
 def test_descriptor_layout_matches_the_header():
-    # int x7, float, int x2, pointer, long long x2 (C layout: 64 bytes, the pointer at 40)
-    assert ctypes.sizeof(fa.FaAttnDesc) == 64
+    # int x7, float, int x2, pointer, long long x2, pointer (C layout: 72 bytes,
+    # the additive mask at 40, the boolean mask at 64)
+    assert ctypes.sizeof(fa.FaAttnDesc) == 72
     assert fa.FaAttnDesc.mask.offset == 40 and fa.FaAttnDesc.mask_stride_h.offset == 56
+    assert fa.FaAttnDesc.bool_mask.offset == 64

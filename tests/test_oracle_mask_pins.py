@@ -112,6 +112,51 @@ def test_causal_shaped_mask_equals_causal_flag():
         assert np.allclose(a[key], b[key], rtol=0, atol=1e-14), key
 
 
+def test_logical_mask_closed_form():
+    # .ag_flash_mask: TRUE (may attend) -> 0, FALSE -> -Inf, elementwise, any shape
+    m = np.array([[True, False, True, True],
+                  [False, False, True, False],
+                  [True, True, True, True]])
+    want = np.array([[0.0, -np.inf, 0.0, 0.0],
+                     [-np.inf, -np.inf, 0.0, -np.inf],
+                     [0.0, 0.0, 0.0, 0.0]])
+    got = oracle.logical_mask_bias(m)
+    assert got.dtype == np.float64 and got.shape == m.shape
+    assert np.array_equal(got, want)
+    assert np.array_equal(oracle.logical_mask_bias(m[None, None]), want[None, None])
+
+
+def test_logical_causal_mask_equals_causal_flag():
+    # the lower-triangular logical mask (key j <= query i allowed) is the causal
+    # rule, so forward and gradients agree with causal=True and no mask
+    q, k, v, do = _case(Hq=2, Hkv=1, Lq=7, Lkv=7, seed=31)
+    m = oracle.logical_mask_bias(np.tril(np.ones((7, 7), dtype=bool)))
+    a = oracle.backward(q, k, v, do, 0.5, True, 0)
+    b = oracle.backward(q, k, v, do, 0.5, False, 0, bias=m)
+    for key in a:
+        assert np.allclose(a[key], b[key], rtol=0, atol=1e-14), key
+
+
+def test_logical_mask_matches_brute_force():
+    q, k, v, do = _case(Lq=5, Lkv=6, seed=32)
+    allowed_pairs = np.random.default_rng(33).random((5, 6)) > 0.3
+    bias = oracle.logical_mask_bias(allowed_pairs)
+    O, L = oracle.forward(q, k, v, 0.6, False, 0, bias=bias)
+    Ob, Lb = _brute(q, k, v, 0.6, False, 0, bias)
+    assert np.abs(O - Ob).max() <= 1e-12
+    assert np.array_equal(np.isneginf(L), np.isneginf(Lb))
+
+
+def test_planted_inverted_logical_mask_is_caught(monkeypatch):
+    # reading TRUE as "blocked" must fail the closed form and the causal pin
+    real = oa.logical_mask_bias
+    monkeypatch.setattr(oracle, "logical_mask_bias", lambda m: real(~np.asarray(m, dtype=bool)))
+    with pytest.raises(AssertionError):
+        test_logical_mask_closed_form()
+    with pytest.raises(AssertionError):
+        test_logical_causal_mask_equals_causal_flag()
+
+
 def test_row_constant_mask_shifts_only_the_lse():
     q, k, v, do = _case(Lq=5, Lkv=6, seed=15)
     c = np.array([0.5, -1.0, 2.0, 0.0, 3.5])
