@@ -93,8 +93,9 @@ def flash_attention(q, k, v, scale: float | None = None, causal: bool = False, w
     window > 0: additionally only keys with i - j < window (plus, without
     causal, every key after i). Returns O (and the natural-log LSE, which
     carries no gradient, when return_lse). mask (optional): float32 additive
-    mask [.., Lq, Lkv] added to the scaled scores (0 attends, -inf blocks; see
-    include/fa.h), the same for the gradient, itself without gradient.
+    mask [.., Lq, Lkv] added to the scaled scores (0 attends, -inf blocks), or
+    a bool mask of that shape, True where the pair may attend (see
+    include/fa.h); the same for the gradient, itself without gradient.
     Raises ValueError for inputs the kernels do not support; nothing is
     computed any other way.
     """
