@@ -134,6 +134,13 @@ template <int S, int NS, class F> __device__ __forceinline__ void unroll_slots(i
 // fragment (left alone, the scheduler serialises read -> wait -> MFMA).
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// dQ with the head dim undivided: 1 computes S^T before dP^T and places the
+// exponentials of S^T between the dP^T MFMAs, 0 interleaves the two products
+// and forms P and dS after both.
+#ifndef FA2_DQ_SPLIT
+#define FA2_DQ_SPLIT 1
+#endif
+
 // Issue priority around the MFMA chains of the forward and dQ kernels (two
 // workgroups share a CU there): the wave in its product phase goes first, the
 // other wave's softmax VALU fills the issue slots in between. In the forward
@@ -638,81 +645,167 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
         const char* kl = smem + (t % NS) * C::STAGEB;
         const char* vl = kl + C::TILEB;
         const int t0 = (t_lo + t) * BKV;
-        // S^T = K Q^T and dP^T = V dO^T in batches of H fragments of each; a
-        // batch's K/V fragments are requested before the previous batch's MFMAs
+        const bool need = (t0 + BKV > a.Lkv) || (a.causal && t0 + BKV - 1 > i0) ||
+                          (a.window && i_last - t0 >= a.window);
         f32x16 s[C::NKB], dp[C::NKB];
-        {
-            constexpr int H = 2, BPK = C::NKG / H, NB = C::NKB * BPK;
-            auto load = [&](int k, u32x4 (&kf)[H], u32x4 (&vf)[H]) {
+        if constexpr (DW == 1 && FA2_DQ_SPLIT) {
+            // S^T = K Q^T first, then dP^T = V dO^T with the exponentials of S^T
+            // placed between its MFMAs; element masks are applied to P afterwards
+            // (one MFMA code path for every tile). Fragments come in batches of FB,
+            // each batch requested before the previous batch's MFMAs.
+            f32x4 m4[C::NKB][4];
+            if constexpr (MASK) {
 #pragma unroll
-                for (int i = 0; i < H; ++i) {
-                    const int off = to.natural(32 * (k / BPK), (k % BPK) * H + i, cb);
-                    kf[i] = ld16(kl + off);
-                    vf[i] = ld16(vl + off);
-                }
+                for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                    for (int qd = 0; qd < 4; ++qd) {
+                        m4[kb][qd] = mask4_l2(mb, row, t0 + 32 * kb + 8 * qd + 4 * h, a.Lq, a.Lkv, a.mvec);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) m4[kb][qd][i] -= lse2;
+                    }
+            }
+            constexpr int FB = C::NKG < 4 ? C::NKG : 4, BPK = C::NKG / FB, NB = C::NKB * BPK;
+            constexpr int EPB = 16 * C::NKB / NB;  // exponentials per dP^T batch
+            auto loadf = [&](const char* base, int k, u32x4 (&f)[FB]) {
+#pragma unroll
+                for (int i = 0; i < FB; ++i) f[i] = ld16(base + to.natural(32 * (k / BPK), (k % BPK) * FB + i, cb));
             };
-            u32x4 kcur[H], vcur[H];
-            load(0, kcur, vcur);
+            u32x4 cur[FB];
+            loadf(kl, 0, cur);
             prio_mfma();
 #pragma unroll
             for (int k = 0; k < NB; ++k) {
-                u32x4 knxt[H], vnxt[H];
-                if (k + 1 < NB) load(k + 1, knxt, vnxt);
+                u32x4 nxt[FB];
+                if (k + 1 < NB) loadf(kl, k + 1, nxt);
+                else loadf(vl, 0, nxt);
                 sched_fence();
-                const int kb = k / BPK, g0 = (k % BPK) * H;
-                if (g0 == 0) {
-                    s[kb] = zero16();
-                    dp[kb] = zero16();
+                const int kb = k / BPK, g0 = (k % BPK) * FB;
+                if (g0 == 0) s[kb] = zero16();
+#pragma unroll
+                for (int i = 0; i < FB; ++i) Mma<T>::nat(s[kb], cur[i], qf[g0 + i]);
+                sched_fence();
+#pragma unroll
+                for (int i = 0; i < FB; ++i) cur[i] = nxt[i];
+            }
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                u32x4 nxt[FB];
+                if (k + 1 < NB) loadf(vl, k + 1, nxt);
+                const int kb = k / BPK, g0 = (k % BPK) * FB;
+                if (g0 == 0) dp[kb] = zero16();
+#pragma unroll
+                for (int i = 0; i < FB; ++i) Mma<T>::nat(dp[kb], cur[i], df[g0 + i]);
+#pragma unroll
+                for (int e = k * EPB; e < (k + 1) * EPB; ++e) {
+                    const int sb = e / 16, r = e % 16;
+                    s[sb][r] = fast_exp2(fmaf(s[sb][r], a.c, MASK ? m4[sb][r >> 2][r & 3] : -lse2));
                 }
 #pragma unroll
-                for (int i = 0; i < H; ++i) {
-                    Mma<T>::nat(s[kb], kcur[i], qf[g0 + i]);
-                    Mma<T>::nat(dp[kb], vcur[i], df[g0 + i]);
+                for (int i = 0; i < FB; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                    __builtin_amdgcn_sched_group_barrier(0x002, 2 * EPB / FB, 0);  // VALU
                 }
                 sched_fence();
                 if (k + 1 < NB) {
 #pragma unroll
+                    for (int i = 0; i < FB; ++i) cur[i] = nxt[i];
+                }
+            }
+            prio_valu();
+            if (need) {
+                // the allowed keys of this lane's row form one run [clo, chi] of the
+                // tile offsets c = 32 kb + 8(r/4) + r%4 (key t0 + 4h + c)
+                const int base = row - t0 - 4 * h;
+                int chi = a.Lkv - t0 - 4 * h - 1;
+                if (a.causal) chi = min(chi, base);
+                const int clo = a.window ? base - a.window + 1 : INT_MIN;
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int cr = 32 * kb + 8 * (r >> 2) + (r & 3);
+                        s[kb][r] = (cr >= clo && cr <= chi) ? s[kb][r] : 0.f;
+                    }
+            }
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[kb][r] *= dp[kb][r] - dl;  // dS^T
+        } else {
+            // S^T = K Q^T and dP^T = V dO^T in batches of H fragments of each; a
+            // batch's K/V fragments are requested before the previous batch's MFMAs
+            {
+                constexpr int H = 2, BPK = C::NKG / H, NB = C::NKB * BPK;
+                auto load = [&](int k, u32x4 (&kf)[H], u32x4 (&vf)[H]) {
+    #pragma unroll
                     for (int i = 0; i < H; ++i) {
-                        kcur[i] = knxt[i];
-                        vcur[i] = vnxt[i];
+                        const int off = to.natural(32 * (k / BPK), (k % BPK) * H + i, cb);
+                        kf[i] = ld16(kl + off);
+                        vf[i] = ld16(vl + off);
+                    }
+                };
+                u32x4 kcur[H], vcur[H];
+                load(0, kcur, vcur);
+                prio_mfma();
+    #pragma unroll
+                for (int k = 0; k < NB; ++k) {
+                    u32x4 knxt[H], vnxt[H];
+                    if (k + 1 < NB) load(k + 1, knxt, vnxt);
+                    sched_fence();
+                    const int kb = k / BPK, g0 = (k % BPK) * H;
+                    if (g0 == 0) {
+                        s[kb] = zero16();
+                        dp[kb] = zero16();
+                    }
+    #pragma unroll
+                    for (int i = 0; i < H; ++i) {
+                        Mma<T>::nat(s[kb], kcur[i], qf[g0 + i]);
+                        Mma<T>::nat(dp[kb], vcur[i], df[g0 + i]);
+                    }
+                    sched_fence();
+                    if (k + 1 < NB) {
+    #pragma unroll
+                        for (int i = 0; i < H; ++i) {
+                            kcur[i] = knxt[i];
+                            vcur[i] = vnxt[i];
+                        }
                     }
                 }
             }
-        }
-        prio_valu();
-        if constexpr (DW > 1) {
-            reduce_partials<DW, C::NKB>(s, red, rw * DW, dw, lane);
-            reduce_partials<DW, C::NKB>(dp, red + RW * DW * C::NKB * 16 * 64, rw * DW, dw, lane);
-        }
+            prio_valu();
+            if constexpr (DW > 1) {
+                reduce_partials<DW, C::NKB>(s, red, rw * DW, dw, lane);
+                reduce_partials<DW, C::NKB>(dp, red + RW * DW * C::NKB * 16 * 64, rw * DW, dw, lane);
+            }
 
-        const bool need = (t0 + BKV > a.Lkv) || (a.causal && t0 + BKV - 1 > i0) ||
-                          (a.window && i_last - t0 >= a.window);
-        f32x4 m4[C::NKB][4];
-        if constexpr (MASK) {
-#pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-                for (int qd = 0; qd < 4; ++qd) {
-                    m4[kb][qd] = mask4_l2(mb, row, t0 + 32 * kb + 8 * qd + 4 * h, a.Lq, a.Lkv, a.mvec);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) m4[kb][qd][i] -= lse2;
-                }
-        }
-        auto dscore = [&](auto masked) {
-#pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float p = fast_exp2(fmaf(s[kb][r], a.c, MASK ? m4[kb][r >> 2][r & 3] : -lse2));
-                    if constexpr (decltype(masked)::value) {
-                        const int j = t0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3), dd = row - j;
-                        p = ((j < a.Lkv) & (dd >= dlo) & (dd < dhi)) ? p : 0.f;
+            f32x4 m4[C::NKB][4];
+            if constexpr (MASK) {
+    #pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+    #pragma unroll
+                    for (int qd = 0; qd < 4; ++qd) {
+                        m4[kb][qd] = mask4_l2(mb, row, t0 + 32 * kb + 8 * qd + 4 * h, a.Lq, a.Lkv, a.mvec);
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i) m4[kb][qd][i] -= lse2;
                     }
-                    s[kb][r] = p * (dp[kb][r] - dl);  // dS^T
-                }
-        };
-        if (need) dscore(std::true_type{});
-        else dscore(std::false_type{});
+            }
+            auto dscore = [&](auto masked) {
+    #pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float p = fast_exp2(fmaf(s[kb][r], a.c, MASK ? m4[kb][r >> 2][r & 3] : -lse2));
+                        if constexpr (decltype(masked)::value) {
+                            const int j = t0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3), dd = row - j;
+                            p = ((j < a.Lkv) & (dd >= dlo) & (dd < dhi)) ? p : 0.f;
+                        }
+                        s[kb][r] = p * (dp[kb][r] - dl);  // dS^T
+                    }
+            };
+            if (need) dscore(std::true_type{});
+            else dscore(std::false_type{});
+        }
         PF<T> pf[C::NPG];
 #pragma unroll
         for (int gg = 0; gg < C::NPG; ++gg) pf[gg] = make_pf<T>(s[gg >> 1], gg & 1);
