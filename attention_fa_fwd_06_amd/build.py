@@ -19,8 +19,6 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-PROBE = os.path.join(PKG, "mfma_ceiling")
-LDS_PROBE = os.path.join(PKG, "lds_ceiling")
 ARCH = "gfx950"
 
 SOURCES = ["fa_api.cpp", "fa_kernels_f32.hip", "fa_kernels_f16.hip", "fa_kernels_bf16.hip"]
@@ -77,13 +75,6 @@ def build(verbose: bool = False, resource_usage: bool = False, defines=(), out: 
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, out)
-    if out == LIB:
-        # measurement helpers: the sustained MFMA rate and LDS read rate of this GPU
-        for src, exe in (("mfma_ceiling.hip", PROBE), ("lds_ceiling.hip", LDS_PROBE)):
-            cmd = [_hipcc(), *COMMON, os.path.join(CSRC, src), "-o", exe]
-            r = subprocess.run(cmd, capture_output=True, text=True)
-            if r.returncode != 0:
-                raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     if verbose or resource_usage:
         for log in logs:
             lines = [ln for ln in log.splitlines() if "packed-fp32-ops" not in ln]

@@ -134,12 +134,6 @@ template <int S, int NS, class F> __device__ __forceinline__ void unroll_slots(i
 // fragment (left alone, the scheduler serialises read -> wait -> MFMA).
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// dQ with the head dim undivided: 1 computes S^T before dP^T and places the
-// exponentials of S^T between the dP^T MFMAs, 0 interleaves the two products
-// and forms P and dS after both.
-#ifndef FA2_DQ_SPLIT
-#define FA2_DQ_SPLIT 1
-#endif
 // K and V fragments per batch in that order (2 measured 0.2488 against 0.2508 ms
 // for 4 at D = 256, the same at D = 128; 8 spills)
 #ifndef FA2_DQ_FB
@@ -155,21 +149,16 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // 5 % faster at D = 256 with the plain priority; the asymmetric form takes the
 // D = 128 forward from 0.1605 to 0.1566 ms (three same-box A/B rounds) and is
 // no better for dQ.
-#ifndef FA2_MFMA_PRIO
-#define FA2_MFMA_PRIO 1
-#endif
 template <bool ASYM = false> __device__ __forceinline__ void prio_mfma() {
-    if constexpr (FA2_MFMA_PRIO && ASYM) {
+    if constexpr (ASYM) {
         const unsigned slot = __builtin_amdgcn_s_getreg(4 | (0 << 6) | (3 << 11));
         if (slot & 1) __builtin_amdgcn_s_setprio(2);
         else __builtin_amdgcn_s_setprio(1);
-    } else if constexpr (FA2_MFMA_PRIO) {
+    } else {
         __builtin_amdgcn_s_setprio(1);
     }
 }
-__device__ __forceinline__ void prio_valu() {
-    if constexpr (FA2_MFMA_PRIO) __builtin_amdgcn_s_setprio(0);
-}
+__device__ __forceinline__ void prio_valu() { __builtin_amdgcn_s_setprio(0); }
 
 // Sum of the two 16-bit values packed in `pk`, added to acc (one v_dot2 with
 // ones): the forward's row sum of the probabilities as they enter the MFMA.
@@ -653,7 +642,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
         const bool need = (t0 + BKV > a.Lkv) || (a.causal && t0 + BKV - 1 > i0) ||
                           (a.window && i_last - t0 >= a.window);
         f32x16 s[C::NKB], dp[C::NKB];
-        if constexpr (DW == 1 && FA2_DQ_SPLIT) {
+        if constexpr (DW == 1) {
             // S^T = K Q^T first, then dP^T = V dO^T with the exponentials of S^T
             // placed between its MFMAs; element masks are applied to P afterwards
             // (one MFMA code path for every tile). Fragments come in batches of FB,
@@ -738,8 +727,10 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[kb][r] *= dp[kb][r] - dl;  // dS^T
         } else {
-            // S^T = K Q^T and dP^T = V dO^T in batches of H fragments of each; a
-            // batch's K/V fragments are requested before the previous batch's MFMAs
+            // d split over DW waves: partial S^T = K Q^T and dP^T = V dO^T over this
+            // wave's d slice in batches of H fragments of each (a batch's K/V
+            // fragments requested before the previous batch's MFMAs), summed
+            // across the slices through LDS
             {
                 constexpr int H = 2, BPK = C::NKG / H, NB = C::NKB * BPK;
                 auto load = [&](int k, u32x4 (&kf)[H], u32x4 (&vf)[H]) {
@@ -1092,13 +1083,15 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_lds_kernel(BwdArgs a
 // score block, so a SIMD runs one wave of each kind. Keys are owned by the
 // workgroup alone (no atomics).
 //
-// Query tiles go through a three-slot LDS ring. Step t first forms the score
-// products of tile t (and, on the dV wave, P); one barrier then publishes P,
-// makes tile t+1 (already landed) visible and frees the slot of tile t-1 for
-// the DMA of tile t+2; after it both waves update their accumulators from
-// tile t. The dV wave issues at a higher priority, so its exp phase runs
-// while the dK wave's products keep the matrix core busy. The LDS fragments
-// of the next product are requested before the MFMAs of the current one.
+// Query tiles go through a three-slot LDS ring with one barrier per tile: it
+// publishes P of tile t, makes tile t+1 (already landed) visible and frees
+// the slot of tile t-1 for the DMA of tile t+2. The dK wave forms dP of tile
+// t before that barrier and dS and its dK update after it. The dV wave runs
+// one tile ahead: after the barrier of tile t it forms the scores of tile
+// t+1, then updates dV from tile t with the exponentials of tile t+1 placed
+// between those MFMAs, and stores P of tile t+1 before the next barrier. The
+// LDS fragments of the next product are requested before the MFMAs of the
+// current one.
 //
 // Under a causal mask without window a workgroup may take key blocks p and
 // nkt-1-p, which gives every workgroup the same amount of work. Workgroups of
@@ -1106,41 +1099,30 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_lds_kernel(BwdArgs a
 // last one down with heads innermost, so the workgroups of a group stream the
 // same Q/dO tiles at about the same time through that XCD's L2.
 // ===========================================================================
-// dV wave of the paired dK/dV kernel (head dim not split): 1 runs it pipelined
-// across query tiles (scores of tile t+1 before the dV update of tile t, with
-// that tile's exponentials between the update's MFMAs), 0 in the plain order.
-#ifndef FA2_DKV_VPIPE
-#define FA2_DKV_VPIPE 1
-#endif
-
-template <class T, int DMAX, int BQ, int KW, int DW> struct DkvPipeCfg {
+template <class T, int DMAX, int BQ, int KW> struct DkvPipeCfg {
     static constexpr int NS = 3;  // tile t (computing), t+1 (landed), t+2 (in flight)
-    static constexpr int NW = 2 * KW * DW, NT = 64 * NW, BKV = 32 * KW;
-    static constexpr int DS = DMAX / DW;                  // head-dim slice of one wave
-    static constexpr int SCH = DS / 8, NKG = DS / 16, NDB = DS / 32;
+    static constexpr int NW = 2 * KW, NT = 64 * NW, BKV = 32 * KW;
+    static constexpr int NKG = DMAX / 16, NDB = DMAX / 32;
     static constexpr int NRB = BQ / 32, NPG = BQ / 16;
     static constexpr int ROWB = DMAX * 2, TILEB = BQ * ROWB;
     static constexpr int ROWSB = 2 * BQ * 4;  // lse and delta of the tile's rows
     static constexpr int STAGEB = 2 * TILEB + ((ROWSB + 1023) / 1024) * 1024;
     static constexpr int PBUF = KW * NPG * 64 * 16;  // P of every key block as MFMA operands, lane-major
-    // partial S / dP of every wave (d split over DW waves), fp32, lane-major
-    static constexpr int XBUF = DW > 1 ? NW * NRB * 16 * 64 * 4 : 0;
-    static constexpr int LDS = NS * STAGEB + 2 * PBUF + XBUF;
+    static constexpr int LDS = NS * STAGEB + 2 * PBUF;
     static_assert(LDS <= kLdsBudget, "dK/dV stages do not fit in LDS");
-    static_assert(DS % 64 == 0 && (BQ == 32 || BQ == 64) && (DW == 1 || DW == 2), "configuration");
+    static_assert(DMAX % 64 == 0 && (BQ == 32 || BQ == 64), "configuration");
 };
 
-template <class T, int DMAX, int BQ, int KW, int DW, int OCC, int PRIO, bool MASK>
-__global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, int pair) {
-    using C = DkvPipeCfg<T, DMAX, BQ, KW, DW>;
+template <class T, int DMAX, int BQ, int KW, int OCC, int PRIO, bool MASK>
+__global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, int pair) {
+    using C = DkvPipeCfg<T, DMAX, BQ, KW>;
     using T8 = typename Vec8<T>::type;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: buffer descriptors below depend on it
     const int h = lane >> 5, ln = lane & 31;
-    const bool vw = w < KW * DW;  // dV wave (else dK wave)
-    const int kw = (w % (KW * DW)) / DW;  // key block of this wave
-    const int dw = w % DW;                // head-dim slice of this wave
+    const bool vw = w < KW;  // dV wave (else dK wave)
+    const int kw = w % KW;   // key block of this wave
     if (PRIO && vw) __builtin_amdgcn_s_setprio(1);
 
     const int nkt = (a.Lkv + C::BKV - 1) / C::BKV;
@@ -1168,15 +1150,9 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
     to.init(lane);
     DmaPlan<BQ, DMAX, C::NW> dma;
     dma.init(lane, w, D);
-    constexpr int WD = KW * DW;  // delta is fetched by the first dK wave, lse by wave 0
+    constexpr int WD = KW;  // delta is fetched by the first dK wave, lse by wave 0
     char* const pbase = smem + C::NS * C::STAGEB + (kw * C::NPG * 64 + lane) * 16;
-    // partial-sum slots: this wave's, and the wave with the other d slice of the same role and key block
-    f32x4* const xown = reinterpret_cast<f32x4*>(smem + C::NS * C::STAGEB + 2 * C::PBUF) + w * C::NRB * 4 * 64 + lane;
-    const f32x4* const xoth = xown + (DW > 1 ? (dw == 0 ? 1 : -1) : 0) * C::NRB * 4 * 64;
-    const int cb = dw * C::SCH;  // chunk base of this wave's d slice
-    // allowed entries: query - key in [dlo, dhi)
-    const int dlo = a.causal ? 0 : INT_MIN;
-    const int dhi = a.window ? a.window : INT_MAX;
+    constexpr int cb = 0;  // chunk base of the tile columns (the head dim is not split)
     const int aoff = vw ? 0 : C::TILEB;  // phase-A operand: Q (dV wave) or dO (dK wave)
     const int toff = vw ? C::TILEB : 0;  // phase-B operand (transposed): dO or Q
 
@@ -1247,7 +1223,7 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
 #pragma unroll
             for (int gi = 0; gi < C::NKG; ++gi) fr0[gi] = ld16(smem + aoff + to.natural(0, gi, cb));
 
-            if constexpr (V && DW == 1 && FA2_DKV_VPIPE) {
+            if constexpr (V) {
                 // dV wave, pipelined across query tiles. After the barrier of tile it
                 // come the score products of tile it+1 (visible since that barrier),
                 // then dV^T += dO^T P of tile it with the exponentials of tile it+1
@@ -1455,20 +1431,21 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
                     }
                 }
             } else {
-            int slot = 0, qt_cur = qt_hi, hq_cnt = 0;
+            // dK wave: dP of tile it, then (after the barrier that publishes the dV
+            // wave's P of that tile) dS = P (dP - Delta) and dK^T += Q^T dS
+            int slot = 0;
             for (int it = 0; it < n_it; ++it) {
                 const char* st = smem + slot * C::STAGEB;
                 const float* lf = reinterpret_cast<const float*>(st + 2 * C::TILEB);
                 const char* tb = st + toff;
-                char* pb = pbase + (it & 1) * C::PBUF;
-                const int q0 = qt_cur * BQ;
+                const char* pb = pbase + (it & 1) * C::PBUF;
 
-                // phase A: S (dV wave) or dP (dK wave) of this tile's rows x this lane's key.
+                // phase A: dP of this tile's rows x this lane's key.
                 // Row block 0's fragments are already here; row block 1's arrive in two
                 // halves, each requested one chain ahead of its use.
                 f32x16 x[C::NRB];
-                u32x4 nx[C::NDB];     // row group 0 of the phase-B operand, all column blocks
-                f32x4 rv[C::NRB][4];  // lse (dV wave) or delta (dK wave) of the rows this lane holds
+                u32x4 nx[C::NDB];     // row group 0 of Q^T, all column blocks
+                f32x4 rv[C::NRB][4];  // delta of the rows this lane holds
                 {
                     constexpr int HG = C::NKG / 2;
                     u32x4 fr1[C::NKG];
@@ -1495,94 +1472,29 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
                         for (int gi = 0; gi < C::NKG; ++gi) Mma<T>::nat(x[1], fr1[gi], bf[gi]);
                     }
                     sched_fence();
-                    const float* rowv = lf + (V ? 0 : BQ) + 4 * h;
+                    const float* rowv = lf + BQ + 4 * h;
 #pragma unroll
                     for (int rb = 0; rb < C::NRB; ++rb)
 #pragma unroll
                         for (int qd = 0; qd < 4; ++qd)
                             rv[rb][qd] = *reinterpret_cast<const f32x4*>(rowv + 32 * rb + 8 * qd);
                 }
-                if constexpr (DW > 1) {
-                    // S (or dP) = sum of the two d slices' partial products, added in
-                    // the same order by both waves, so both hold identical bits
+                // dP - Delta while the dV wave is still on its exp phase
 #pragma unroll
-                    for (int rb = 0; rb < C::NRB; ++rb)
+                for (int rb = 0; rb < C::NRB; ++rb)
 #pragma unroll
-                        for (int qd = 0; qd < 4; ++qd)
-                            xown[(rb * 4 + qd) * 64] = f32x4{x[rb][4 * qd], x[rb][4 * qd + 1], x[rb][4 * qd + 2],
-                                                             x[rb][4 * qd + 3]};
-                    lds_barrier();  // partials visible
-#pragma unroll
-                    for (int rb = 0; rb < C::NRB; ++rb)
-#pragma unroll
-                        for (int qd = 0; qd < 4; ++qd) {
-                            const f32x4 o = xoth[(rb * 4 + qd) * 64];
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const float mine = x[rb][4 * qd + i];
-                                x[rb][4 * qd + i] = dw == 0 ? mine + o[i] : o[i] + mine;
-                            }
-                        }
-                }
-
-                PF<T> pf[C::NPG];
-                if constexpr (V) {
-                    // P = exp2(c S - log2(e) lse), masked entries 0; x[rb][4 qd + i] is
-                    // row 32 rb + 8 qd + 4 h + i of the tile
-                    if constexpr (MASK) {
-                        // log2(e) (mask - lse) of each element; rows without any allowed key
-                        // get -inf
-                        const MaskRow mb = mask_slice(a, b, g * reps + hq_cnt);
-#pragma unroll
-                        for (int rb = 0; rb < C::NRB; ++rb)
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                const int irow = q0 + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
-                                rv[rb][r >> 2][r & 3] =
-                                    mask_l2(mb, irow, key, a.Lq, a.Lkv) - lse_l2_masked(rv[rb][r >> 2][r & 3]);
-                            }
-                    }
-                    auto probs = [&](auto masked) {
-#pragma unroll
-                        for (int rb = 0; rb < C::NRB; ++rb)
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                float p = fast_exp2(fmaf(x[rb][r], a.c, MASK ? rv[rb][r >> 2][r & 3]
-                                                                              : -rv[rb][r >> 2][r & 3] * kLog2e));
-                                if constexpr (decltype(masked)::value) {
-                                    const int irow = q0 + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3), dd = irow - key;
-                                    p = ((irow < a.Lq) & (dd >= dlo) & (dd < dhi)) ? p : 0.f;
-                                }
-                                x[rb][r] = p;
-                            }
-                    };
-                    const bool need = (q0 + BQ > a.Lq) || (a.causal && j0 + C::BKV - 1 > q0) ||
-                                      (a.window && min(q0 + BQ, a.Lq) - 1 - j0 >= a.window);
-                    if (need) probs(std::true_type{});
-                    else probs(std::false_type{});
-#pragma unroll
-                    for (int gg = 0; gg < C::NPG; ++gg) {
-                        pf[gg] = make_pf<T>(x[gg >> 1], gg & 1);
-                        if (DW == 1 || dw == 0) st16(pb + gg * 1024, pf[gg].v);
-                    }
-                } else {
-                    // dP - Delta while the dV wave is still on its exp phase
-#pragma unroll
-                    for (int rb = 0; rb < C::NRB; ++rb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) x[rb][r] -= rv[rb][r >> 2][r & 3];
-                }
+                    for (int r = 0; r < 16; ++r) x[rb][r] -= rv[rb][r >> 2][r & 3];
                 wait_vm<0>();   // this wave's share of tile it+1
                 lds_barrier();  // P visible; tile it+1 visible; every wave is done with tile it-1
                 if (it + 2 < n_it) issue();
 
-                // phase B: acc[db] += (dO or Q)^T (column block db, row group gg) x
-                // (P or dS) of row group gg, row groups outermost so that the NDB
-                // accumulator chains alternate. The next row group's fragments (after
-                // the last group: the next tile's phase-A fragments) are requested
-                // ahead of each group's MFMAs; the dK wave forms dS = P (dP - Delta)
-                // one row group ahead.
+                // phase B: acc[db] += Q^T (column block db, row group gg) x dS of row
+                // group gg, row groups outermost so that the NDB accumulator chains
+                // alternate. The next row group's fragments (after the last group: the
+                // next tile's phase-A fragments) are requested ahead of each group's
+                // MFMAs; dS = P (dP - Delta) is formed one row group ahead.
                 const int nslot = slot == C::NS - 1 ? 0 : slot + 1;
+                PF<T> pf[C::NPG];
                 auto ds_group = [&](int gg) {
                     const T8 pv = __builtin_bit_cast(T8, ld16(pb + gg * 1024));
                     const int rb = gg >> 1, hf = gg & 1;
@@ -1593,7 +1505,7 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
                     }
                     pf[gg] = make_pf<T>(x[rb], hf);
                 };
-                if constexpr (!V) ds_group(0);
+                ds_group(0);
 #pragma unroll
                 for (int gg = 0; gg < C::NPG; ++gg) {
                     u32x4 nn[C::NDB];
@@ -1609,9 +1521,7 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
                     sched_fence();
 #pragma unroll
                     for (int db = 0; db < C::NDB; ++db) Mma<T>::nat(acc[db], nx[db], pf[gg].v);
-                    if constexpr (!V) {
-                        if (gg + 1 < C::NPG) ds_group(gg + 1);
-                    }
+                    if (gg + 1 < C::NPG) ds_group(gg + 1);
                     sched_fence();
                     if (gg + 1 < C::NPG) {
 #pragma unroll
@@ -1619,10 +1529,6 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
                     }
                 }
                 slot = nslot;
-                if (++hq_cnt == reps) {
-                    hq_cnt = 0;
-                    --qt_cur;
-                }
             }
             }
 
@@ -1633,7 +1539,7 @@ __global__ __launch_bounds__(128 * KW * DW, OCC) void fa_dkv_pipe_kernel(BwdArgs
                 for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
                     for (int qd = 0; qd < 4; ++qd) {
-                        const int d = dw * C::DS + 32 * db + 8 * qd + 4 * h;
+                        const int d = 32 * db + 8 * qd + 4 * h;
                         if (d < Do)
                             store4<T>(op + d, acc[db][4 * qd] * sc, acc[db][4 * qd + 1] * sc,
                                       acc[db][4 * qd + 2] * sc, acc[db][4 * qd + 3] * sc);
@@ -1688,11 +1594,11 @@ hipError_t launch_dkv2(const BwdArgs& a, hipStream_t s) {
 // without window; it is used only while it still leaves a workgroup for each
 // of the 256 CUs.
 constexpr int kPairMinGrid = 256;
-template <class T, int DMAX, int BQ, int KW, int DW, int OCC, int PRIO>
+template <class T, int DMAX, int BQ, int KW, int OCC, int PRIO>
 hipError_t launch_dkv_pipe(const BwdArgs& a, hipStream_t s) {
-    using C = DkvPipeCfg<T, DMAX, BQ, KW, DW>;
-    auto kern = (a.mask || a.bmask) ? fa_dkv_pipe_kernel<T, DMAX, BQ, KW, DW, OCC, PRIO, true>
-                       : fa_dkv_pipe_kernel<T, DMAX, BQ, KW, DW, OCC, PRIO, false>;
+    using C = DkvPipeCfg<T, DMAX, BQ, KW>;
+    auto kern = (a.mask || a.bmask) ? fa_dkv_pipe_kernel<T, DMAX, BQ, KW, OCC, PRIO, true>
+                       : fa_dkv_pipe_kernel<T, DMAX, BQ, KW, OCC, PRIO, false>;
     hipError_t e = set_lds(kern, C::LDS);
     if (e != hipSuccess) return e;
     const long long nkt = (a.Lkv + C::BKV - 1) / C::BKV;
@@ -1738,17 +1644,16 @@ inline int dmax16(int D) { return D <= 64 ? 64 : D <= 128 ? 128 : D <= 256 ? 256
 #define FA2_DKV_512 32, 1, 4, 1, 2
 #endif
 
-// dK/dV on wave pairs: <query tile, key blocks of 32, waves splitting d, min waves per SIMD,
-// dV-wave priority>. At D = 256 (one wave per SIMD) the raised priority measured
+// dK/dV on wave pairs: <query tile, key blocks of 32, min waves per SIMD, dV-wave priority>. At D = 256 (one wave per SIMD) the raised priority measured
 // 0.3375 against 0.3351 ms without it on the windowed 8192-token workload.
 #ifndef FA2_DKVS_64
-#define FA2_DKVS_64 64, 4, 1, 2, 1
+#define FA2_DKVS_64 64, 4, 2, 1
 #endif
 #ifndef FA2_DKVS_128
-#define FA2_DKVS_128 64, 4, 1, 2, 1
+#define FA2_DKVS_128 64, 4, 2, 1
 #endif
 #ifndef FA2_DKVS_256
-#define FA2_DKVS_256 32, 2, 1, 1, 0
+#define FA2_DKVS_256 32, 2, 1, 0
 #endif
 
 }  // namespace lds

@@ -13,14 +13,10 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long-running oracle check")
 
 
-def pytest_collection_modifyitems(config, items):
-    # Print the case name before each GPU test so that a run that dies on the
-    # GPU still says which case it was running.
-    pass
-
-
 @pytest.fixture(autouse=True)
 def _announce(request):
+    # Print the case name before each GPU test, so that a run that dies on the
+    # GPU still says which case it was running.
     if request.node.get_closest_marker("gpu") is not None:
         print(f"\n[gpu-case] {request.node.nodeid}", flush=True)
     yield
