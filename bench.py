@@ -1,10 +1,15 @@
 """Benchmark: fwd+bwd attention TFLOP/s and % of bf16 dense MFMA peak on one MI355X.
 
 One step = fa_fwd -> fa_bwd_preprocess -> fa_bwd_dkv -> fa_bwd_dq on inputs
-already resident in HBM (the whole hot path, through the C ABI). W untimed
-warm-up steps, then K timed steps bracketed by synchronisation; HIP events on
-the stream the kernels are launched on give the step time and, in a second
-timed pass, each kernel's average duration.
+already resident in HBM (the whole hot path, through the C ABI). First a
+clock-settle phase (back-to-back steps for --settle-ms of wall time: the
+chip's clocks take some 50-100 ms of sustained work to come up), then W
+untimed warm-up steps, then K timed steps bracketed by synchronisation; HIP
+events on the stream the kernels are launched on give the step time and, in
+a second timed pass, each kernel's average duration. The settle phase's
+length is part of the printed line. The GFX clock is sampled (amdsmi, when
+available) during the two timed passes, and the MFMA peak is also given at
+that measured clock.
 
 FLOP count (algorithmic): N = allowed (i, j) pairs per (batch, head), exactly
 counted from the mask; forward = 4*D*N*B*Hq, backward = 2.5 x forward.
@@ -95,7 +100,70 @@ def workload_bytes(w):
             "dq": 3 * q + 2 * kv + 2 * row}
 
 
-def time_gpu(w, steps: int, warmup: int):
+class ClockSampler:
+    """Samples the GPU's GFX clock (MHz) from a host thread through amdsmi while
+    started; `summary()` is None when amdsmi is unavailable or gives no
+    reading."""
+
+    def __init__(self):
+        self.samples, self.error, self._h, self._stop, self._thr = [], None, None, None, None
+        try:
+            import amdsmi
+            import torch
+
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if len(handles) == 1:
+                self._h = handles[0]
+            else:  # match the PCI bus of HIP device 0
+                bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+                for h in handles:
+                    bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+                    if bus is not None and int(bdf.split(":")[1], 16) == int(bus):
+                        self._h = h
+            if self._h is None:
+                self.error = "no amdsmi handle for HIP device 0"
+            self._smi = amdsmi
+        except Exception as e:  # pragma: no cover - depends on the box
+            self.error = f"amdsmi unavailable: {type(e).__name__}"
+
+    def _read(self):
+        info = self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.GFX)
+        return float(info["clk"])
+
+    def start(self):
+        if self._h is None:
+            return
+        import threading
+
+        self._stop = threading.Event()
+
+        def loop():
+            while not self._stop.is_set():
+                try:
+                    self.samples.append(self._read())
+                except Exception as e:  # pragma: no cover
+                    self.error = f"amdsmi read failed: {type(e).__name__}"
+                    return
+                self._stop.wait(0.002)
+
+        self._thr = threading.Thread(target=loop, daemon=True)
+        self._thr.start()
+
+    def stop(self):
+        if self._thr is not None:
+            self._stop.set()
+            self._thr.join()
+            self._thr = None
+
+    def summary(self):
+        if not self.samples:
+            return None
+        x = self.samples
+        return {"mean": round(sum(x) / len(x), 1), "min": min(x), "max": max(x), "samples": len(x)}
+
+
+def time_gpu(w, steps: int, warmup: int, settle_ms: float = 300.0, clock: ClockSampler | None = None):
     import torch
 
     import attention_fa_fwd_06_amd as fa
@@ -123,6 +191,16 @@ def time_gpu(w, steps: int, warmup: int):
         for _, f in kernels:
             f()
 
+    # clock settle: back-to-back steps until settle_ms of wall time has passed
+    torch.cuda.synchronize()
+    s0, n_settle = time.perf_counter(), 0
+    while (time.perf_counter() - s0) * 1e3 < settle_ms:
+        for _ in range(4):
+            step()
+        n_settle += 4
+        torch.cuda.synchronize()
+    settle = {"ms": round((time.perf_counter() - s0) * 1e3, 1), "steps": n_settle}
+
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -130,6 +208,9 @@ def time_gpu(w, steps: int, warmup: int):
     stream = torch.cuda.current_stream(dev)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    if clock is not None:
+        clock.samples = []
+        clock.start()
     wall0 = time.perf_counter()
     t0.record(stream)
     for _ in range(steps):
@@ -149,44 +230,68 @@ def time_gpu(w, steps: int, warmup: int):
             b.record(stream)
             ev[name].append((a, b))
     torch.cuda.synchronize()
+    if clock is not None:
+        clock.stop()
     per = {name: sum(a.elapsed_time(b) for a, b in pairs) / len(pairs) for name, pairs in ev.items()}
-    return ms_step, wall * 1e3 / steps, per
+    return ms_step, wall * 1e3 / steps, per, settle
 
 
-def cpu_baseline(w, budget_s: float = 12.0):
-    """The float64 oracle on a bounded sample of the workload: whole (batch,
-    kv-group) slices, run until about budget_s seconds have been spent."""
-    import numpy as np
+def cpu_baseline(w, budget_s: float = 12.0, max_workers: int = 16):
+    """The float64 oracle (oracle.backward as it stands) on a bounded sample of
+    the workload, on the host's cores.
+
+    The unit of work is one (batch, kv-group) slice: the full forward and
+    backward of the group's query heads against its K and V. Slices run in a
+    thread pool of one worker per available core (at most max_workers, BLAS
+    held to one thread per worker), in waves of one slice per worker, until
+    about budget_s of wall time has been spent. When a whole slice would take
+    longer than about half the budget on one core (the 8192- and 32768-token
+    workloads), each slice is cut to its first n query rows and keys (n at
+    least twice the window, when there is one): under a
+    causal mask those rows attend only to those keys, so the cut slice is a
+    smaller instance of the same problem, and its work is counted exactly.
+    Reported in TFLOP/s on the same algorithmic count as the GPU figure."""
+    import concurrent.futures as cf
+
+    from threadpoolctl import threadpool_limits
 
     import oracle
     from synth import decode, workload_inputs
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    x = workload_inputs(w)
+    cores = max(1, min(max_workers, len(os.sched_getaffinity(0))))
     reps = w.Hq // w.Hkv
-    done, flops, t_total = 0, 0.0, 0.0
-    groups = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
-    per_head = workload_flops(w)["total"] / (w.B * w.Hq)
-    for b, g in groups:
+    # the oracle materialises every score: about 12 D FLOP per (row, key, head)
+    # at roughly 1e10 FLOP/s on one core
+    # (a cut slice keeps at least twice the window, so the window still trims it)
+    n, n_min = w.Lq, max(64, min(w.Lq, 2 * w.window))
+    while n // 2 >= n_min and 12.0 * n * n * w.D * reps / 1e10 > budget_s / 2:
+        n //= 2
+    cut = n < w.Lq
+    Lq, Lkv = (n, min(n, w.Lkv)) if cut else (w.Lq, w.Lkv)
+    x = workload_inputs(w)
+    pairs = allowed_pairs(Lq, Lkv, w.causal, w.window)
+    per_slice = 3.5 * 4.0 * w.D * pairs * reps
+
+    def one(bg):
+        b, g = bg
         hs = slice(g * reps, (g + 1) * reps)
-        args = [decode(x["q"][b:b + 1, hs], w.dtype), decode(x["k"][b:b + 1, g:g + 1], w.dtype),
-                decode(x["v"][b:b + 1, g:g + 1], w.dtype), decode(x["do"][b:b + 1, hs], w.dtype)]
-        t = time.perf_counter()
+        args = [decode(x["q"][b:b + 1, hs, :Lq], w.dtype), decode(x["k"][b:b + 1, g:g + 1, :Lkv], w.dtype),
+                decode(x["v"][b:b + 1, g:g + 1, :Lkv], w.dtype), decode(x["do"][b:b + 1, hs, :Lq], w.dtype)]
         oracle.backward(*args, w.scale, w.causal, w.window)
-        t_total += time.perf_counter() - t
-        done += 1
-        flops += per_head * reps
-        if t_total >= budget_s:
-            break
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {len(groups)} (batch, kv-group) slices ({done * reps} of {w.B * w.Hq} query heads), "
-                      f"full fwd+bwd in float64, {t_total:.2f} s",
-            "seconds": t_total}
+
+    groups = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+    done, t0 = 0, time.perf_counter()
+    with threadpool_limits(limits=1, user_api="blas"), cf.ThreadPoolExecutor(cores) as ex:
+        while done < len(groups) and time.perf_counter() - t0 < budget_s:
+            wave = groups[done:done + cores]
+            list(ex.map(one, wave))
+            done += len(wave)
+    secs = time.perf_counter() - t0
+    what = f"first {Lq} query rows and {Lkv} keys of " if cut else ""
+    return {"value": done * per_slice / secs / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{what}{done} of {len(groups)} (batch, kv-group) slices ({done * reps} of {w.B * w.Hq} "
+                      f"query heads), full fwd+bwd in float64, {cores} threads, {secs:.2f} s",
+            "seconds": secs}
 
 
 def roofline(kernel: str, flops: float, nbytes: float, ms: float, peak_tflops: float) -> dict:
@@ -202,12 +307,24 @@ def roofline(kernel: str, flops: float, nbytes: float, ms: float, peak_tflops: f
             "frac": achieved / PEAK_HBM_GBS}
 
 
-def run(w, steps, warmup, with_cpu):
+def _r4(d):
+    return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
+
+
+def _cpu_line(cb):
+    cb = dict(cb)
+    cb["value"] = float(f"{cb['value']:.4g}")
+    cb["seconds"] = round(cb["seconds"], 2)
+    return cb
+
+
+def run(w, steps, warmup, settle_ms, cpu_budget, clock):
     f = workload_flops(w)
     by = workload_bytes(w)
-    ms, wall_ms, per = time_gpu(w, steps, warmup)
+    ms, wall_ms, per, settle = time_gpu(w, steps, warmup, settle_ms, clock)
     tflops = f["total"] / (ms * 1e-3) / 1e12
     peak = PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+    clk = clock.summary() if clock is not None else None
     res = {
         "workload": w,
         "ms_per_step": ms,
@@ -220,20 +337,37 @@ def run(w, steps, warmup, with_cpu):
         "bwd_ms": per["fa_bwd_preprocess"] + per["fa_bwd_dkv"] + per["fa_bwd_dq"],
         "flops": f,
         "bytes": by,
+        "settle": settle,
+        "clock": clk,
     }
+    unit_flops = {"fa_fwd": f["fwd"], "fa_bwd_dkv": f["dkv"], "fa_bwd_dq": f["dq"]}
+    unit_bytes = {"fa_fwd": by["fwd"], "fa_bwd_dkv": by["dkv"], "fa_bwd_dq": by["dq"]}
+    # one roofline entry per MFMA kernel; the line's `roofline` is the dominant one
+    res["kernels"] = {}
+    for n in ("fa_fwd", "fa_bwd_dkv", "fa_bwd_dq"):
+        e = roofline(n, unit_flops[n], unit_bytes[n], per[n], peak)
+        e.update({"traffic": measured_traffic(w.name, n), "algorithmic_bytes": unit_bytes[n], "avg_ms": per[n]})
+        if clk is not None and e["bound"] == "mfma":
+            e["frac_at_measured_clock"] = e["achieved"] / (peak * clk["mean"] / 2400.0)
+        res["kernels"][n] = e
     dom = max(("fa_fwd", "fa_bwd_dkv", "fa_bwd_dq"), key=lambda n: per[n])
-    unit_flops = {"fa_fwd": f["fwd"], "fa_bwd_dkv": f["dkv"], "fa_bwd_dq": f["dq"]}[dom]
-    dom_bytes = {"fa_fwd": by["fwd"], "fa_bwd_dkv": by["dkv"], "fa_bwd_dq": by["dq"]}[dom]
-    res["roofline"] = roofline(dom, unit_flops, dom_bytes, per[dom], peak)
-    res["roofline"].update({"traffic": measured_traffic(w.name, dom),
-                            "traffic_unit": "HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
-                            "algorithmic_bytes": dom_bytes, "avg_ms": per[dom]})
-    res["kernel_tflops"] = {n: unit_flops_n / (per[n] * 1e-3) / 1e12 for n, unit_flops_n in
-                            (("fa_fwd", f["fwd"]), ("fa_bwd_dkv", f["dkv"]), ("fa_bwd_dq", f["dq"]))}
+    res["roofline"] = dict(res["kernels"][dom])
+    res["roofline"]["traffic_unit"] = "HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)"
+    res["kernel_tflops"] = {n: unit_flops[n] / (per[n] * 1e-3) / 1e12 for n in unit_flops}
     res["pre_gbs"] = by["pre"] / (per["fa_bwd_preprocess"] * 1e-3) / 1e9
-    if with_cpu:
-        res["cpu_baseline"] = cpu_baseline(w)
+    if cpu_budget > 0:
+        res["cpu_baseline"] = cpu_baseline(w, cpu_budget)
     return res
+
+
+def _clock_fields(r, peak):
+    clk = r["clock"]
+    if clk is None:
+        return {"gfx_clock_mhz": None, "peak_at_measured_clock": None, "pct_of_peak_at_measured_clock": None}
+    # the published dense peak is 256 CUs x 4096 FLOP per clock at 2.4 GHz
+    pk = peak * clk["mean"] / 2400.0
+    return {"gfx_clock_mhz": clk, "peak_at_measured_clock": round(pk, 1),
+            "pct_of_peak_at_measured_clock": round(100.0 * r["tflops"] / pk, 3)}
 
 
 def main(argv=None):
@@ -242,11 +376,15 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=100)
     # The chip's clocks take some 50-100 ms of back-to-back steps to settle
     # (a 2048-token step runs 0.89 ms over its first 25 steps, 0.67 ms from
-    # about step 75 on), so the default warm-up covers well over that.
+    # about step 75 on): the settle phase runs before the counted warm-up.
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="wall time of back-to-back steps run before the counted warm-up (clock settle)")
     ap.add_argument("--workload", type=int, default=2, help="index into synth.WORKLOADS (default: the 2048-token GQA)")
-    ap.add_argument("--also", type=str, default="0,1,3,5", help="comma list of extra workload indices reported inline")
+    ap.add_argument("--also", type=str, default="0,1,3,4,5", help="comma list of extra workload indices reported inline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for the main workload")
+    ap.add_argument("--also-cpu-budget", type=float, default=6.0, help="seconds of oracle time per extra workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain elementwise copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args(argv)
@@ -270,25 +408,35 @@ def main(argv=None):
         torch.cuda.synchronize()
         del x, y
 
+    clock = ClockSampler()
     w = WORKLOADS[args.workload]
-    main_res = run(w, args.steps, args.warmup, not args.no_cpu_baseline)
+    cpu_main = 0.0 if args.no_cpu_baseline else args.cpu_budget
+    cpu_also = 0.0 if args.no_cpu_baseline else args.also_cpu_budget
+    main_res = run(w, args.steps, args.warmup, args.settle_ms, cpu_main, clock)
     extra = {}
     for idx in [int(s) for s in args.also.split(",") if s.strip() != ""]:
         if idx == args.workload:
             continue
-        r = run(WORKLOADS[idx], args.steps, args.warmup, False)
+        wx = WORKLOADS[idx]
+        r = run(wx, args.steps, args.warmup, args.settle_ms, cpu_also, clock)
         wb = r["bytes"]
-        extra[WORKLOADS[idx].name] = {
+        extra[wx.name] = {
             "ms_per_step": round(r["ms_per_step"], 4), "tflops": round(r["tflops"], 2),
             # algorithmic HBM bytes of the four kernels over the step time (the
             # small cases are launch- and latency-bound, not MFMA-bound)
             "hbm_gbs": round((wb["fwd"] + wb["pre"] + wb["dkv"] + wb["dq"]) / (r["ms_per_step"] * 1e-3) / 1e9, 1),
             "tflops_formula": round(r["tflops_formula"], 2), "pct_peak": round(r["pct_peak"], 2),
             "per_kernel_ms": {k: round(v, 4) for k, v in r["per_kernel_ms"].items()},
-            "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r["roofline"].items()},
+            "roofline": _r4(r["roofline"]),
+            "kernels": {k: _r4(v) for k, v in r["kernels"].items()},
+            "clock_settle": r["settle"],
+            **_clock_fields(r, PEAK_FP32_TFLOPS if wx.dtype == "f32" else PEAK_BF16_TFLOPS),
         }
+        if "cpu_baseline" in r:
+            extra[wx.name]["cpu_baseline"] = _cpu_line(r["cpu_baseline"])
 
     r = main_res
+    peak = PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
     line = {
         "metric": METRIC,
         "value": round(r["tflops"], 3),
@@ -296,6 +444,7 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle": r["settle"],
         "ms_per_step": round(r["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -305,21 +454,19 @@ def main(argv=None):
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Lq": w.Lq, "Lkv": w.Lkv, "D": w.D,
                    "causal": w.causal, "window": w.window, "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(r["pct_peak"], 3),
+        **_clock_fields(r, peak),
         "tflops_formula_count": round(r["tflops_formula"], 3),
         "fwd_ms": round(r["fwd_ms"], 4),
         "bwd_ms": round(r["bwd_ms"], 4),
         "per_kernel_ms": {k: round(v, 4) for k, v in r["per_kernel_ms"].items()},
         "kernel_tflops": {k: round(v, 2) for k, v in r["kernel_tflops"].items()},
         "preprocess_gbs": round(r["pre_gbs"], 1),
-        "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r["roofline"].items()},
-        "cpu_baseline": r.get("cpu_baseline"),
+        "roofline": _r4(r["roofline"]),
+        "kernels": {k: _r4(v) for k, v in r["kernels"].items()},
+        "cpu_baseline": _cpu_line(r["cpu_baseline"]) if "cpu_baseline" in r else None,
+        "clock_sampler_error": clock.error,
         "also": extra,
     }
-    if line["cpu_baseline"] is not None:
-        cb = dict(line["cpu_baseline"])
-        cb["value"] = float(f"{cb['value']:.4g}")
-        cb["seconds"] = round(cb["seconds"], 2)
-        line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)
 
 

@@ -4,6 +4,7 @@ from .attention import (  # noqa: F401
     backward,
     bwd_preprocess,
     forward,
+    key_grads,
     key_span,
     logical_mask_bias,
     mask_matrix,

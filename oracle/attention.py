@@ -262,3 +262,57 @@ def sample_keys(q, k, v, do, scale, causal, window, b, g, keys):
             dK[n] += scale * (dS[:, jc] @ q[b, h, rows])
             dV[n] += P[:, jc] @ dOr
     return {"dK": dK, "dV": dV}
+
+
+def key_grads(q, k, v, do, scale, causal, window, b, g, keys, row_block=256, workers=1):
+    """dK, dV [len(keys), D] of the given keys of kv head g in batch b, over query-row blocks.
+
+    For each query head h of the group (increasing h) and each block of up to
+    row_block consecutive query rows among those that may attend one of the
+    keys: the rows' scores over the key span that holds all of their allowed
+    keys (exact, since masked probabilities are 0), their LSE, P, O and
+    Delta = rowsum(dO * O); then, for the requested keys, dP = dO V^T,
+    dS = P (dP - Delta) and the contributions scale * dS^T Q to dK and P^T dO
+    to dV. The contributions are added in (head, block) order whatever
+    `workers` is; workers > 1 evaluates the blocks on that many threads (the
+    matrix products and ufuncs release the interpreter lock), with the BLAS
+    library held to one thread each.
+    """
+    Hq, Hkv, Lq, Lkv = q.shape[1], k.shape[1], q.shape[2], k.shape[2]
+    reps = Hq // Hkv
+    _kv_head(g * reps, Hq, Hkv)  # checks Hq % Hkv
+    keys = np.asarray(keys, dtype=np.int64)
+    Kg, Vg = k[b, g], v[b, g]
+    sees = mask_matrix(np.arange(Lq), Lkv, causal, window, cols=keys).any(axis=1)
+    rows_any = np.nonzero(sees)[0]
+    blocks = [rows_any[i:i + row_block] for i in range(0, len(rows_any), row_block)]
+    tasks = [(h, rows) for h in range(g * reps, (g + 1) * reps) for rows in blocks]
+
+    def contribution(task):
+        h, rows = task
+        cols = key_span(rows, Lkv, causal, window)  # contiguous keys cols[0] .. cols[-1]
+        _, P, O, _ = rows_forward(q[b, h, rows], Kg, Vg, rows, scale, causal, window, cols)
+        dOr = np.asarray(do[b, h, rows], dtype=np.float64)
+        delta = bwd_preprocess(O, dOr)
+        pos = keys - cols[0]
+        inside = (pos >= 0) & (pos < len(cols))
+        Pk = np.zeros((len(rows), len(keys)))
+        Pk[:, inside] = P[:, pos[inside]]  # keys outside the span are masked for every row
+        dS = Pk * (dOr @ Vg[keys].T - delta[:, None])
+        return scale * (dS.T @ q[b, h, rows]), Pk.T @ dOr
+
+    dK = np.zeros((len(keys), Kg.shape[1]))
+    dV = np.zeros((len(keys), Vg.shape[1]))
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+
+        from threadpoolctl import threadpool_limits
+
+        with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(workers) as ex:
+            parts = list(ex.map(contribution, tasks))
+    else:
+        parts = map(contribution, tasks)
+    for pk, pv in parts:
+        dK += pk
+        dV += pv
+    return {"dK": dK, "dV": dV}

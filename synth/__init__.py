@@ -117,6 +117,30 @@ def make_inputs(B, Hq, Hkv, Lq, Lkv, D, dtype, seed, sigma_qkv=1.0, sigma_do=1.0
     return {"q": q, "k": k, "v": v, "do": do}
 
 
+def make_spiked_inputs(B, Hq, Hkv, Lq, Lkv, D, dtype, seed, period=100, offset=100, height=6.5, sigma_qk=0.35,
+                       Dv=None):
+    """Inputs whose scores (under the default scale 1/sqrt(D)) have a flat floor
+    and isolated high keys, for exercising a running maximum that grows.
+
+    q, k, v and dO are drawn as in make_inputs (q and k with sigma_qk, v and dO
+    with sigma 1); then component 0 of every q row is set to 1 and component 0
+    of key j to height * sqrt(D) for the keys j = offset, offset + period, ...
+    (else 0), so the score of those keys stands about `height` (natural-log
+    units) above the others, whose spread is about sigma_qk**2. Values are
+    rounded to the storage dtype after the change, like every other input."""
+    Dv = D if Dv is None else Dv
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = {}
+    for name, shape, sigma in (("q", (B, Hq, Lq, D), sigma_qk), ("k", (B, Hkv, Lkv, D), sigma_qk),
+                               ("v", (B, Hkv, Lkv, Dv), 1.0), ("do", (B, Hq, Lq, Dv), 1.0)):
+        x[name] = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(sigma)
+    x["q"][..., 0] = 1.0
+    j = np.arange(Lkv)
+    spike = (j >= offset) & ((j - offset) % period == 0)
+    x["k"][..., 0] = np.where(spike, np.float32(height * math.sqrt(D)), np.float32(0.0))
+    return {name: encode(val, dtype) for name, val in x.items()}
+
+
 def workload_inputs(w: Workload):
     return make_inputs(w.B, w.Hq, w.Hkv, w.Lq, w.Lkv, w.D, w.dtype, w.seed, w.sigma_qkv, w.sigma_do)
 

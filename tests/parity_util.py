@@ -78,3 +78,33 @@ def compare_full(B, Hq, Hkv, Lq, Lkv, D, dtype, causal, window, seed, sigma_qkv=
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, f"parity above {tol}: {bad} (all: {errs})"
     return errs
+
+
+def run_gpu_masked(t: dict, scale: float, causal: bool, window: int, mask=None):
+    """The four calls with an optional mask tensor (float32 additive or bool)."""
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    o, lse = fa.forward(q, k, v, scale, causal, window, mask=mask)
+    B, Hq, Lq, _ = q.shape
+    delta = torch.empty((B, Hq, Lq), device=q.device, dtype=torch.float32)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, scale, causal, window, delta=delta, mask=mask)
+    torch.cuda.synchronize()
+    return {"O": o, "LSE": lse, "Delta": delta, "dQ": dq, "dK": dk, "dV": dv}
+
+
+def compare_given(x: dict, dtype: str, scale: float, causal: bool, window: int, mask=None, tol=None):
+    """Whole-tensor parity of all six outputs on the given storage arrays.
+
+    mask: None, a float32 array (additive: 0 attends, -inf blocks) or a bool
+    array (True attends), broadcastable to [B, Hq, Lq, Lkv]. Returns the errors."""
+    bias = None
+    if mask is not None:
+        bias = oracle.logical_mask_bias(mask) if mask.dtype == np.bool_ else mask.astype(np.float64)
+    ref = oracle.backward(*(decode(x[n], dtype) for n in ("q", "k", "v", "do")), scale, causal, window, bias=bias)
+    mt = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask)).cuda()
+    got = to_f64(run_gpu_masked(gpu_inputs(x, dtype), scale, causal, window, mt), dtype)
+    check_finite(got, ref["LSE"])
+    tol = TOL[dtype] if tol is None else tol
+    errs = {key: rel_err(got[key], ref[key]) for key in ("O", "LSE", "Delta", "dQ", "dK", "dV")}
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"parity above {tol}: {bad} (all: {errs})"
+    return errs

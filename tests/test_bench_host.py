@@ -65,3 +65,28 @@ def test_roofline_bound_follows_the_machine_balance():
     r = bench.roofline("fa_fwd", f["fwd"], by["fwd"], 0.01, bench.PEAK_BF16_TFLOPS)
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
     assert abs(r["achieved"] - by["fwd"] / 0.01e-3 / 1e9) < 1e-6
+
+
+def test_cpu_baseline_on_a_small_workload():
+    # the oracle timed on whole slices of the 256-token workload, threads reported
+    r = bench.cpu_baseline(WORKLOADS[1], budget_s=1.0)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["value"] > 0
+    assert 1 <= r["cores"] <= min(16, len(os.sched_getaffinity(0)))
+    assert "slices" in r["sample"]
+
+
+def test_cpu_baseline_cuts_a_large_slice_to_a_prefix(monkeypatch):
+    # the 8192-token windowed workload: a slice is cut to its first rows and keys,
+    # at least twice the window
+    import oracle as orc
+
+    seen = {}
+
+    def fake_backward(q, k, v, do, scale, causal, window):
+        seen["shape"] = (q.shape, k.shape, causal, window)
+
+    monkeypatch.setattr(orc, "backward", fake_backward)
+    r = bench.cpu_baseline(WORKLOADS[3], budget_s=0.5)
+    (qs, ks, causal, window) = seen["shape"]
+    assert qs[2] == ks[2] == 2048 and causal and window == 1024
+    assert r["sample"].startswith("first 2048 query rows and 2048 keys")

@@ -10,6 +10,8 @@ slices; the 8192- and 32768-token workloads are run whole in the launch
 configuration the benchmark times and compared on sampled rows and keys
 (the oracle computes those one by one), plus identities that hold at any size.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -110,8 +112,21 @@ def test_workload_bf16_gqa8_L32768():
     got = to_f64(run_gpu(gpu_inputs(x, w.dtype), w.scale, w.causal, w.window), w.dtype)
     check_finite(got)
     rows = [0, 1, 127, 128, 4095, 16383, 16384, 30001, 32767]
-    keys = [32767, 32766, 32704, 32703, 32640, 32600]
-    _sampled_check(w, x, got, [(0, 0), (0, 13), (0, 31)], rows, [(0, 0), (0, 3)], keys)
+    _sampled_check(w, x, got, [(0, 0), (0, 13), (0, 31)], rows, [], [])
+    # dK/dV element-wise over the whole key range of two kv groups: the first,
+    # middle and last 128-key blocks whole (under the causal key-block pairing
+    # the middle two are one workgroup's pair, the first and last another's),
+    # plus keys scattered in between; each from every query row of the group's
+    # eight heads (the oracle's row-blocked key gradients)
+    keys = np.concatenate([np.arange(0, 128), np.arange(16256, 16512), np.arange(32640, 32768),
+                           [1000, 4095, 4096, 8191, 8192, 12345, 20000, 24575, 24576, 30000]])
+    q, k, v, do = (decode(x[n], w.dtype) for n in ("q", "k", "v", "do"))
+    workers = min(16, len(os.sched_getaffinity(0)))
+    for g in (0, 3):
+        ref = oracle.key_grads(q, k, v, do, w.scale, w.causal, w.window, 0, g, keys, workers=workers)
+        for key in ("dK", "dV"):
+            e = rel_err(got[key][0, g, keys], ref[key])
+            assert e <= w.tol, (key, g, e)
     _identities(w, x, got)
 
 
@@ -203,6 +218,16 @@ def test_zero_and_negative_scale(scale):
     compare_full(2, 2, 1, 90, 70, 64, "f16", False, 0, seed=27, scale=scale)
     compare_full(1, 8, 2, 5, 300, 128, "bf16", True, 0, seed=28, scale=scale)
     compare_full(1, 2, 2, 40, 40, 32, "f32", True, 7, seed=29, scale=scale)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,L,D,dtype", [(8, 16, 8, 850, 128, "bf16"), (8, 8, 8, 1100, 64, "f16"),
+                                                 (8, 8, 8, 420, 256, "bf16")])
+def test_causal_key_block_pairing_with_odd_block_count(B, Hq, Hkv, L, D, dtype):
+    # Under a causal mask without window the dK/dV workgroups take key blocks p
+    # and nkt-1-p when that still leaves 256 workgroups. Here the number of key
+    # blocks (128 keys, 64 at D = 256) is odd (7, 9, 7), so the middle block runs
+    # alone, and the last block is ragged.
+    compare_full(B, Hq, Hkv, L, L, D, dtype, True, 0, seed=30 + D)
 
 
 def test_deterministic():

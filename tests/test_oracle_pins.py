@@ -446,3 +446,67 @@ def test_key_span_holds_every_allowed_key():
         for i in range(Lq):
             span = oracle.key_span([i], Lkv, causal, window)
             assert set(np.nonzero(ok[i])[0]) <= set(span.tolist())
+
+
+# ---------------------------------------------------------------------------
+# row-blocked key gradients (used for the 32768-token workload's dK/dV)
+# ---------------------------------------------------------------------------
+
+KEY_GRAD_SHAPES = [
+    # B, Hq, Hkv, Lq, Lkv, causal, window
+    (2, 4, 2, 37, 37, True, 0),
+    (1, 6, 2, 40, 40, True, 5),
+    (1, 4, 1, 20, 33, False, 0),
+    (2, 4, 2, 30, 12, True, 3),  # rows with no allowed key
+    (1, 2, 2, 25, 25, False, 7),
+]
+
+
+def _key_grads_agree():
+    """key_grads against the full backward (whole score matrices, no blocking) on
+    small shapes, for every kv head, all keys and a scattered subset, with row
+    blocks of 1, 5 and 64 rows and 1 or 3 threads; True when all agree to 1e-12
+    (an exception counts as disagreement)."""
+    try:
+        return _key_grads_agree_or_raise()
+    except Exception:
+        return False
+
+
+def _key_grads_agree_or_raise():
+    for n, (B, Hq, Hkv, Lq, Lkv, causal, window) in enumerate(KEY_GRAD_SHAPES):
+        q, k, v, do = _case(B, Hq, Hkv, Lq, Lkv, 5, seed=40 + n)
+        r = oracle.backward(q, k, v, do, 0.45, causal, window)
+        for keys in (np.arange(Lkv), np.array([Lkv - 1, 0, Lkv // 2, 1])):
+            for row_block, workers in ((1, 1), (5, 3), (64, 1)):
+                for b in range(B):
+                    for g in range(Hkv):
+                        s = oracle.key_grads(q, k, v, do, 0.45, causal, window, b, g, keys, row_block, workers)
+                        if np.abs(s["dK"] - r["dK"][b, g, keys]).max() > 1e-12:
+                            return False
+                        if np.abs(s["dV"] - r["dV"][b, g, keys]).max() > 1e-12:
+                            return False
+    return True
+
+
+def test_key_grads_match_the_full_backward():
+    assert _key_grads_agree()
+
+
+@pytest.mark.parametrize("mistake", ["span_short_by_one", "rows_of_one_head"])
+def test_key_grads_planted_mistakes_are_caught(monkeypatch, mistake):
+    if mistake == "span_short_by_one":
+        # each row block's LSE taken without the first key of its span
+        real = oa.key_span
+        monkeypatch.setattr(oa, "key_span", lambda rows, Lkv, causal, window: real(rows, Lkv, causal, window)[1:])
+    elif mistake == "rows_of_one_head":
+        # every query head of the group handled with the rows of the group's first head
+        real_kg = oa.key_grads
+
+        def kg(q, k, v, do, scale, causal, window, b, g, keys, row_block=256, workers=1):
+            reps = q.shape[1] // k.shape[1]
+            q1 = q.copy()
+            q1[:, g * reps:(g + 1) * reps] = q[:, g * reps:g * reps + 1]
+            return real_kg(q1, k, v, do, scale, causal, window, b, g, keys, row_block, workers)
+        monkeypatch.setattr(oracle, "key_grads", kg)
+    assert not _key_grads_agree()
