@@ -7,8 +7,10 @@ chip's clocks take some 50-100 ms of sustained work to come up), then W
 untimed warm-up steps, then K timed steps bracketed by synchronisation; HIP
 events on the stream the kernels are launched on give the step time and, in
 a second timed pass, each kernel's average duration. The settle phase's
-length is part of the printed line. The GFX clock is sampled (amdsmi, when
-available) during the two timed passes, and the MFMA peak is also given at
+length is part of the printed line. After the timed passes the workload runs
+back to back for another --clock-ms of wall time while a host thread samples
+the GFX clock (amdsmi, when available; its reading is refreshed too slowly
+for the short timed passes themselves), and the MFMA peak is also given at
 that measured clock.
 
 FLOP count (algorithmic): N = allowed (i, j) pairs per (batch, head), exactly
@@ -157,13 +159,14 @@ class ClockSampler:
             self._thr = None
 
     def summary(self):
-        if not self.samples:
+        x = [c for c in self.samples if c >= 100.0]  # a reading of 0 is no reading
+        if not x:
             return None
-        x = self.samples
         return {"mean": round(sum(x) / len(x), 1), "min": min(x), "max": max(x), "samples": len(x)}
 
 
-def time_gpu(w, steps: int, warmup: int, settle_ms: float = 300.0, clock: ClockSampler | None = None):
+def time_gpu(w, steps: int, warmup: int, settle_ms: float = 300.0, clock: ClockSampler | None = None,
+             clock_ms: float = 1000.0):
     import torch
 
     import attention_fa_fwd_06_amd as fa
@@ -208,9 +211,6 @@ def time_gpu(w, steps: int, warmup: int, settle_ms: float = 300.0, clock: ClockS
     stream = torch.cuda.current_stream(dev)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    if clock is not None:
-        clock.samples = []
-        clock.start()
     wall0 = time.perf_counter()
     t0.record(stream)
     for _ in range(steps):
@@ -230,9 +230,18 @@ def time_gpu(w, steps: int, warmup: int, settle_ms: float = 300.0, clock: ClockS
             b.record(stream)
             ev[name].append((a, b))
     torch.cuda.synchronize()
-    if clock is not None:
-        clock.stop()
     per = {name: sum(a.elapsed_time(b) for a, b in pairs) / len(pairs) for name, pairs in ev.items()}
+
+    # clock under sustained load of this workload (not part of any timing)
+    if clock is not None and clock_ms > 0:
+        clock.samples = []
+        clock.start()
+        c0 = time.perf_counter()
+        while (time.perf_counter() - c0) * 1e3 < clock_ms:
+            for _ in range(4):
+                step()
+            torch.cuda.synchronize()
+        clock.stop()
     return ms_step, wall * 1e3 / steps, per, settle
 
 
@@ -318,10 +327,10 @@ def _cpu_line(cb):
     return cb
 
 
-def run(w, steps, warmup, settle_ms, cpu_budget, clock):
+def run(w, steps, warmup, settle_ms, cpu_budget, clock, clock_ms=1000.0):
     f = workload_flops(w)
     by = workload_bytes(w)
-    ms, wall_ms, per, settle = time_gpu(w, steps, warmup, settle_ms, clock)
+    ms, wall_ms, per, settle = time_gpu(w, steps, warmup, settle_ms, clock, clock_ms)
     tflops = f["total"] / (ms * 1e-3) / 1e12
     peak = PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
     clk = clock.summary() if clock is not None else None
@@ -380,6 +389,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="wall time of back-to-back steps run before the counted warm-up (clock settle)")
+    ap.add_argument("--clock-ms", type=float, default=1000.0,
+                    help="wall time of back-to-back steps, after the timed passes, over which the GFX clock is sampled")
     ap.add_argument("--workload", type=int, default=2, help="index into synth.WORKLOADS (default: the 2048-token GQA)")
     ap.add_argument("--also", type=str, default="0,1,3,4,5", help="comma list of extra workload indices reported inline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -412,13 +423,13 @@ def main(argv=None):
     w = WORKLOADS[args.workload]
     cpu_main = 0.0 if args.no_cpu_baseline else args.cpu_budget
     cpu_also = 0.0 if args.no_cpu_baseline else args.also_cpu_budget
-    main_res = run(w, args.steps, args.warmup, args.settle_ms, cpu_main, clock)
+    main_res = run(w, args.steps, args.warmup, args.settle_ms, cpu_main, clock, args.clock_ms)
     extra = {}
     for idx in [int(s) for s in args.also.split(",") if s.strip() != ""]:
         if idx == args.workload:
             continue
         wx = WORKLOADS[idx]
-        r = run(wx, args.steps, args.warmup, args.settle_ms, cpu_also, clock)
+        r = run(wx, args.steps, args.warmup, args.settle_ms, cpu_also, clock, args.clock_ms)
         wb = r["bytes"]
         extra[wx.name] = {
             "ms_per_step": round(r["ms_per_step"], 4), "tflops": round(r["tflops"], 2),
