@@ -93,6 +93,13 @@ template <int ROWB> __device__ __forceinline__ int swz(int r) {
     }
 }
 
+// LDS pitch of a tile row for head-dim bucket DMAX (16-bit elements): the
+// swizzle needs rows of 128 bytes or a multiple of 256, so the 32 and 96
+// buckets store rows of 64 and 128 elements; the padding chunks are filled
+// with zeros by the DMA and never read, and every product still runs over
+// DMAX columns only.
+constexpr int tile_row_bytes(int DMAX) { return DMAX <= 64 ? 128 : (DMAX + 127) / 128 * 256; }
+
 // Wait until at most N vector-memory operations of this wave are in flight
 // (lgkm and export counters left unconstrained).
 template <int N> __device__ __forceinline__ void wait_vm() {
@@ -222,9 +229,11 @@ template <int ROWB> struct TileOffs {
 
 // LDS-DMA plan for an R x DMAX (16-bit) tile issued by NW waves: wave w owns
 // instructions w, w + NW, ...; instruction i fills bytes [1024 i, 1024 i + 1024)
-// of the tile with the 64 chunks whose swizzled position falls there.
+// of the tile with the 64 chunks whose swizzled position falls there (chunks
+// past the head dim, including a padded row's, read as zero).
 template <int R, int DMAX, int NW> struct DmaPlan {
-    static constexpr int NDC = DMAX / 8;
+    static constexpr int ROWB = tile_row_bytes(DMAX);
+    static constexpr int NDC = ROWB / 16;
     static constexpr int NI = R * NDC / 64;
     static_assert(R * NDC % 64 == 0 && NI % NW == 0, "tile must split evenly into 1 KiB DMA pieces per wave");
     static constexpr int NIW = NI / NW;
@@ -234,7 +243,7 @@ template <int R, int DMAX, int NW> struct DmaPlan {
         for (int n = 0; n < NIW; ++n) {
             const int slot = 64 * (w + n * NW) + lane;
             const int r = slot / NDC, p = slot % NDC;
-            const int c = p ^ swz<DMAX * 2>(r);  // logical chunk stored at physical chunk p
+            const int c = p ^ swz<ROWB>(r);  // logical chunk stored at physical chunk p
             voff[n] = (c * 8 < D) ? (uint32_t)((r * D + c * 8) * 2) : kOob;
         }
     }
@@ -251,7 +260,7 @@ template <int R, int DMAX, int NW> struct DmaPlan {
         for (int n = 0; n < NIW; ++n) {
             const int slot = 64 * (w + n * NW) + lane;
             const int r = slot / NDC, p = slot % NDC;
-            const int c = p ^ swz<DMAX * 2>(r);
+            const int c = p ^ swz<ROWB>(r);
             const uint32_t off = (c * 8 < Dx) ? (uint32_t)(((r + row0) * Dx + c * 8) * 2) : kOob;
             dma16(rs, tile + (w + n * NW) * 1024, off);
         }
@@ -295,11 +304,11 @@ template <class T, int DMAX, int BKV, int RW, int DW, int NS> struct Fwd2Cfg {
     static constexpr int NW = RW * DW, NT = 64 * NW, BQ = 32 * RW;
     static constexpr int DS = DMAX / DW, SCH = DS / 8, NKG = SCH / 2, NDB = DS / 32;
     static constexpr int NKB = BKV / 32, NPG = BKV / 16;
-    static constexpr int ROWB = DMAX * 2, TILEB = BKV * ROWB, STAGEB = 2 * TILEB;
+    static constexpr int ROWB = tile_row_bytes(DMAX), TILEB = BKV * ROWB, STAGEB = 2 * TILEB;
     static constexpr int RED = DW > 1 ? RW * DW * NKB * 16 * 64 * 4 : 0;
     static constexpr int LDS = NS * STAGEB + RED;
     static_assert(LDS <= kLdsBudget, "forward stages do not fit in LDS");
-    static_assert(NS >= 2 && DMAX % 64 == 0 && DS % 32 == 0, "configuration");
+    static_assert(NS >= 2 && DMAX % 32 == 0 && DS % 32 == 0, "configuration");
 };
 
 template <class T, int DMAX, int BKV, int RW, int DW, int OCC, int NS, bool MASK>
@@ -546,11 +555,11 @@ template <class T, int DMAX, int BKV, int RW, int DW, int NS> struct Dq2Cfg {
     static constexpr int NW = RW * DW, NT = 64 * NW, BQ = 32 * RW;
     static constexpr int DS = DMAX / DW, SCH = DS / 8, NKG = SCH / 2, NDB = DS / 32;
     static constexpr int NKB = BKV / 32, NPG = BKV / 16;
-    static constexpr int ROWB = DMAX * 2, TILEB = BKV * ROWB, STAGEB = 2 * TILEB;
+    static constexpr int ROWB = tile_row_bytes(DMAX), TILEB = BKV * ROWB, STAGEB = 2 * TILEB;
     static constexpr int RED = DW > 1 ? 2 * RW * DW * NKB * 16 * 64 * 4 : 0;
     static constexpr int LDS = NS * STAGEB + RED;
     static_assert(LDS <= kLdsBudget, "dQ stages do not fit in LDS");
-    static_assert(NS >= 2 && DMAX % 64 == 0 && DS % 32 == 0, "configuration");
+    static_assert(NS >= 2 && DMAX % 32 == 0 && DS % 32 == 0, "configuration");
 };
 
 // VP: the value head dim differs from D (extended calls); the other
@@ -659,7 +668,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
                     }
             }
             constexpr int FB = C::NKG < FA2_DQ_FB ? C::NKG : FA2_DQ_FB, BPK = C::NKG / FB, NB = C::NKB * BPK;
-            constexpr int EPB = 16 * C::NKB / NB;  // exponentials per dP^T batch
+            constexpr int NSC = 16 * C::NKB, EPB = (NSC + NB - 1) / NB;  // exponentials per dP^T batch
             auto loadf = [&](const char* base, int k, u32x4 (&f)[FB]) {
 #pragma unroll
                 for (int i = 0; i < FB; ++i) f[i] = ld16(base + to.natural(32 * (k / BPK), (k % BPK) * FB + i, cb));
@@ -690,7 +699,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
 #pragma unroll
                 for (int i = 0; i < FB; ++i) Mma<T>::nat(dp[kb], cur[i], df[g0 + i]);
 #pragma unroll
-                for (int e = k * EPB; e < (k + 1) * EPB; ++e) {
+                for (int e = k * EPB; e < (k + 1) * EPB && e < NSC; ++e) {
                     const int sb = e / 16, r = e % 16;
                     s[sb][r] = fast_exp2(fmaf(s[sb][r], a.c, MASK ? m4[sb][r >> 2][r & 3] : -lse2));
                 }
@@ -855,7 +864,7 @@ template <class T, int DMAX, int BQ, int KW, int DW, int NS> struct Dkv2Cfg {
     static constexpr int NW = KW * DW, NT = 64 * NW, BKV = 32 * KW;
     static constexpr int DS = DMAX / DW, SCH = DS / 8, NKG = SCH / 2, NDB = DS / 32;
     static constexpr int NRB = BQ / 32, NPG = BQ / 16;
-    static constexpr int ROWB = DMAX * 2, TILEB = BQ * ROWB;
+    static constexpr int ROWB = tile_row_bytes(DMAX), TILEB = BQ * ROWB;
     static constexpr int ROWSB = 2 * BQ * 4;                    // lse and delta of the tile's rows
     static constexpr int STAGEB = 2 * TILEB + ((ROWSB + 1023) / 1024) * 1024;
     static constexpr int RED1 = DW > 1 ? KW * DW * NRB * 16 * 64 * 4 : 0;
@@ -865,7 +874,7 @@ template <class T, int DMAX, int BQ, int KW, int DW, int NS> struct Dkv2Cfg {
     static constexpr int RED = SEQ ? RED1 : 2 * RED1;
     static constexpr int LDS = NS * STAGEB + RED;
     static_assert(LDS <= kLdsBudget, "dK/dV stages do not fit in LDS");
-    static_assert(NS >= 2 && DMAX % 64 == 0 && DS % 32 == 0 && BQ >= 32 && BQ <= 64, "configuration");
+    static_assert(NS >= 2 && DMAX % 32 == 0 && DS % 32 == 0 && BQ >= 32 && BQ <= 64, "configuration");
 };
 
 template <class T, int DMAX, int BQ, int KW, int DW, int OCC, int NS, bool MASK>
@@ -1104,13 +1113,13 @@ template <class T, int DMAX, int BQ, int KW> struct DkvPipeCfg {
     static constexpr int NW = 2 * KW, NT = 64 * NW, BKV = 32 * KW;
     static constexpr int NKG = DMAX / 16, NDB = DMAX / 32;
     static constexpr int NRB = BQ / 32, NPG = BQ / 16;
-    static constexpr int ROWB = DMAX * 2, TILEB = BQ * ROWB;
+    static constexpr int ROWB = tile_row_bytes(DMAX), TILEB = BQ * ROWB;
     static constexpr int ROWSB = 2 * BQ * 4;  // lse and delta of the tile's rows
     static constexpr int STAGEB = 2 * TILEB + ((ROWSB + 1023) / 1024) * 1024;
     static constexpr int PBUF = KW * NPG * 64 * 16;  // P of every key block as MFMA operands, lane-major
     static constexpr int LDS = NS * STAGEB + 2 * PBUF;
     static_assert(LDS <= kLdsBudget, "dK/dV stages do not fit in LDS");
-    static_assert(DMAX % 64 == 0 && (BQ == 32 || BQ == 64), "configuration");
+    static_assert(DMAX % 32 == 0 && (BQ == 32 || BQ == 64), "configuration");
 };
 
 template <class T, int DMAX, int BQ, int KW, int OCC, int PRIO, bool MASK>
@@ -1609,15 +1618,24 @@ hipError_t launch_dkv_pipe(const BwdArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Head-dim buckets of the 16-bit path: a tile row must be a multiple of 128
-// bytes for the swizzle, so D is served by 64, 128, 256 or 512 (columns past
-// D read as zero and are never stored).
-inline int dmax16(int D) { return D <= 64 ? 64 : D <= 128 ? 128 : D <= 256 ? 256 : 512; }
+// Head-dim buckets of the 16-bit path: D is served by the smallest of 32, 64,
+// 96, 128, 256 and 512 that holds it (columns past D read as zero and are
+// never stored; the 32 and 96 buckets keep padded LDS rows, see
+// tile_row_bytes, but run their products over 32 and 96 columns).
+inline int dmax16(int D) {
+    return D <= 32 ? 32 : D <= 64 ? 64 : D <= 96 ? 96 : D <= 128 ? 128 : D <= 256 ? 256 : 512;
+}
 
 // <tile, waves along rows/keys, waves along d, min waves per SIMD, stages>.
 // Overridable at build time for tuning sweeps (e.g. -DFA2_FWD_128=64,4,1,2,2).
+#ifndef FA2_FWD_32
+#define FA2_FWD_32 64, 4, 1, 2, 2
+#endif
 #ifndef FA2_FWD_64
 #define FA2_FWD_64 64, 4, 1, 2, 2
+#endif
+#ifndef FA2_FWD_96
+#define FA2_FWD_96 64, 4, 1, 2, 2
 #endif
 #ifndef FA2_FWD_128
 #define FA2_FWD_128 64, 4, 1, 2, 2
@@ -1628,8 +1646,14 @@ inline int dmax16(int D) { return D <= 64 ? 64 : D <= 128 ? 128 : D <= 256 ? 256
 #ifndef FA2_FWD_512
 #define FA2_FWD_512 32, 1, 4, 1, 2
 #endif
+#ifndef FA2_DQ_32
+#define FA2_DQ_32 64, 4, 1, 2, 2
+#endif
 #ifndef FA2_DQ_64
 #define FA2_DQ_64 64, 4, 1, 2, 2
+#endif
+#ifndef FA2_DQ_96
+#define FA2_DQ_96 64, 4, 1, 2, 2
 #endif
 #ifndef FA2_DQ_128
 #define FA2_DQ_128 64, 4, 1, 2, 2
@@ -1646,8 +1670,14 @@ inline int dmax16(int D) { return D <= 64 ? 64 : D <= 128 ? 128 : D <= 256 ? 256
 
 // dK/dV on wave pairs: <query tile, key blocks of 32, min waves per SIMD, dV-wave priority>. At D = 256 (one wave per SIMD) the raised priority measured
 // 0.3375 against 0.3351 ms without it on the windowed 8192-token workload.
+#ifndef FA2_DKVS_32
+#define FA2_DKVS_32 64, 4, 2, 1
+#endif
 #ifndef FA2_DKVS_64
 #define FA2_DKVS_64 64, 4, 2, 1
+#endif
+#ifndef FA2_DKVS_96
+#define FA2_DKVS_96 64, 4, 2, 1
 #endif
 #ifndef FA2_DKVS_128
 #define FA2_DKVS_128 64, 4, 2, 1
