@@ -1104,9 +1104,9 @@ __global__ __launch_bounds__(64 * KW * DW, OCC) void fa_dkv_lds_kernel(BwdArgs a
 //
 // Under a causal mask without window a workgroup may take key blocks p and
 // nkt-1-p, which gives every workgroup the same amount of work. Workgroups of
-// one (batch, kv head) are placed on one XCD, and query tiles run from the
-// last one down with heads innermost, so the workgroups of a group stream the
-// same Q/dO tiles at about the same time through that XCD's L2.
+// one (batch, kv head) are placed on one XCD, and the query tiles are walked
+// (heads innermost) in an order under which the workgroups of a group stream
+// the same Q/dO tiles at about the same time through that XCD's L2.
 // ===========================================================================
 template <class T, int DMAX, int BQ, int KW> struct DkvPipeCfg {
     static constexpr int NS = 3;  // tile t (computing), t+1 (landed), t+2 (in flight)
@@ -1192,16 +1192,32 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
             const int i_lo = a.causal ? j0 : 0;
             const int i_hi = a.window ? min(a.Lq - 1, j_last + a.window - 1) : a.Lq - 1;
             const int qt_lo = i_lo / BQ, qt_hi = i_hi / BQ;
-            const int n_it = i_hi >= i_lo ? (qt_hi - qt_lo + 1) * reps : 0;
+            const int nq = qt_hi - qt_lo + 1;
+            const int n_it = i_hi >= i_lo ? nq * reps : 0;
 
-            // tiles in the order (query tile from qt_hi down) x (head of the group)
-            int hq_issue = g * reps, qt_issue = qt_hi, slot_issue = 0;
+            // Tiles in the order (query tile) x (head of the group), the query tiles
+            // walked so that the workgroups of one kv head, which run at the same
+            // pace, visit the same tile at about the same time and share it in L2:
+            // under a causal mask without window every range ends at the last tile,
+            // so all walk down from it; without causal mask every range starts at
+            // tile 0, so all walk up from it; under causal + window the ranges have
+            // the same length nq and different starts, so each walks up from the tile
+            // whose index is a multiple of nq, wrapping to its first tile (at step s
+            // every workgroup is on a tile congruent to s mod nq).
+            const int tdir = a.causal && !a.window ? -1 : 1;
+            const int trot = a.causal && a.window && nq > 0 ? (nq - qt_lo % nq) % nq : 0;
+            auto tile_of = [&](int st) {  // query tile at position st of the walk
+                int u = st + trot;
+                if (u >= nq) u -= nq;
+                return tdir < 0 ? qt_hi - u : qt_lo + u;
+            };
+            int hq_issue = g * reps, st_issue = 0, slot_issue = 0;
             auto issue = [&]() {
                 const size_t qrow0 = (size_t)(b * a.Hq + hq_issue) * a.Lq;
                 const dsc_t rq = make_dsc(reinterpret_cast<const T*>(a.q) + qrow0 * D, qbytes);
                 const dsc_t rdo = make_dsc(reinterpret_cast<const T*>(a.dO) + qrow0 * Dv, obytes);
                 char* st = smem + slot_issue * C::STAGEB;
-                const int qrow = qt_issue * BQ;
+                const int qrow = tile_of(st_issue) * BQ;
                 dma.issue(rq, lds_of(st, smem), qrow, D, w);
                 if (Dv == D) dma.issue(rdo, lds_of(st + C::TILEB, smem), qrow, D, w);
                 else dma.issue_pitch(rdo, lds_of(st + C::TILEB, smem), qrow, Dv, w, lane);
@@ -1216,7 +1232,7 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
                 }
                 if (++hq_issue == (g + 1) * reps) {
                     hq_issue = g * reps;
-                    --qt_issue;
+                    ++st_issue;
                 }
                 slot_issue = slot_issue == C::NS - 1 ? 0 : slot_issue + 1;
             };
@@ -1245,7 +1261,7 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
                 f32x16 x[C::NRB];
                 u32x4 nx[C::NDB];  // dO^T fragments of the row group multiplied next
                 u32x4 px;          // P of that row group (operand of the dV update)
-                int qa = qt_hi, ha = 0;  // query tile and head (in the group) of the next scores
+                int sa = 0, ha = 0;  // walk position and head (in the group) of the next scores
 
                 // S = Q K^T of the tile whose phase-A operand is at `sa`; row block 0's
                 // fragments are in fr0
@@ -1326,7 +1342,7 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
                 auto next_tile = [&]() {
                     if (++ha == reps) {
                         ha = 0;
-                        --qa;
+                        ++sa;
                     }
                 };
                 // dO^T fragments of row group gg of the tile whose dO is at `tb`
@@ -1338,7 +1354,7 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
 
                 // first tile: scores, P stored for the dK wave, its first dO^T row group
                 if (n_it > 0) {
-                    const int q0 = qa * BQ, hq = g * reps + ha;
+                    const int q0 = tile_of(sa) * BQ, hq = g * reps + ha;
                     scores(smem + aoff);
                     u32x4 pn[C::NPG];
 #pragma unroll
@@ -1366,7 +1382,7 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
                     lds_barrier();  // P of tile it visible; tile it+1 visible; tile it-1 done
                     if (it + 2 < n_it) issue();
                     px = ld16(pcur);
-                    const int q0 = qa * BQ, hq = g * reps + ha;
+                    const int q0 = tile_of(sa) * BQ, hq = g * reps + ha;
 #pragma unroll
                     for (int gi = 0; gi < C::NKG; ++gi) fr0[gi] = ld16(sn + aoff + to.natural(0, gi, cb));
                     sched_fence();

@@ -101,8 +101,21 @@ def test_workload_bf16_gqa8_window1024_L8192_D256():
     got = to_f64(run_gpu(gpu_inputs(x, w.dtype), w.scale, w.causal, w.window), w.dtype)
     check_finite(got)
     rows = [0, 1, 31, 32, 63, 64, 127, 1000, 1023, 1024, 1025, 1056, 2047, 4097, 8000, 8190, 8191]
-    keys = [0, 1, 31, 32, 1023, 1024, 3000, 7167, 7168, 8191]
-    _sampled_check(w, x, got, [(0, 0), (0, 7), (0, 8), (0, 15)], rows, [(0, 0), (0, 1)], keys)
+    _sampled_check(w, x, got, [(0, 0), (0, 7), (0, 8), (0, 15)], rows, [], [])
+    # dK/dV element-wise on whole 64-key blocks (one dK/dV workgroup each) at the
+    # start, around the first window length, in the middle and at the end of the
+    # sequence, plus scattered keys, for both kv groups; each key from every query
+    # row of the group's eight heads that may attend it (the oracle's row-blocked
+    # key gradients)
+    keys = np.concatenate([np.arange(0, 64), np.arange(960, 1088), np.arange(4096, 4160), np.arange(8128, 8192),
+                           [3000, 5555, 7167, 7168]])
+    q, k, v, do = (decode(x[n], w.dtype) for n in ("q", "k", "v", "do"))
+    workers = min(16, len(os.sched_getaffinity(0)))
+    for g in (0, 1):
+        ref = oracle.key_grads(q, k, v, do, w.scale, w.causal, w.window, 0, g, keys, workers=workers)
+        for key in ("dK", "dV"):
+            e = rel_err(got[key][0, g, keys], ref[key])
+            assert e <= w.tol, (key, g, e)
     _identities(w, x, got)
 
 
