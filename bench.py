@@ -194,14 +194,20 @@ def time_gpu(w, steps: int, warmup: int, settle_ms: float = 300.0, clock: ClockS
         for _, f in kernels:
             f()
 
-    # clock settle: back-to-back steps until settle_ms of wall time has passed
+    # Clock settle: back-to-back steps until settle_ms of wall time has passed.
+    # Each batch between synchronizations holds about 20 ms of GPU work (sized
+    # from the batches before it), so that the queue never runs dry while the
+    # host enqueues the next one.
     torch.cuda.synchronize()
-    s0, n_settle = time.perf_counter(), 0
+    s0, n_settle, batch = time.perf_counter(), 0, 4
     while (time.perf_counter() - s0) * 1e3 < settle_ms:
-        for _ in range(4):
+        b0 = time.perf_counter()
+        for _ in range(batch):
             step()
-        n_settle += 4
         torch.cuda.synchronize()
+        n_settle += batch
+        per_step = (time.perf_counter() - b0) / batch
+        batch = max(4, min(10000, int(0.02 / max(per_step, 1e-6))))
     settle = {"ms": round((time.perf_counter() - s0) * 1e3, 1), "steps": n_settle}
 
     for _ in range(warmup):
@@ -234,11 +240,12 @@ def time_gpu(w, steps: int, warmup: int, settle_ms: float = 300.0, clock: ClockS
 
     # clock under sustained load of this workload (not part of any timing)
     if clock is not None and clock_ms > 0:
+        batch = max(4, min(10000, int(20.0 / max(ms_step, 1e-3))))  # about 20 ms of GPU work per batch
         clock.samples = []
         clock.start()
         c0 = time.perf_counter()
         while (time.perf_counter() - c0) * 1e3 < clock_ms:
-            for _ in range(4):
+            for _ in range(batch):
                 step()
             torch.cuda.synchronize()
         clock.stop()
