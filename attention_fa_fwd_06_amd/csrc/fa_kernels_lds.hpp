@@ -1199,12 +1199,17 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
             // walked so that the workgroups of one kv head, which run at the same
             // pace, visit the same tile at about the same time and share it in L2:
             // under a causal mask without window every range ends at the last tile,
-            // so all walk down from it; without causal mask every range starts at
-            // tile 0, so all walk up from it; under causal + window the ranges have
-            // the same length nq and different starts, so each walks up from the tile
-            // whose index is a multiple of nq, wrapping to its first tile (at step s
-            // every workgroup is on a tile congruent to s mod nq).
-            const int tdir = a.causal && !a.window ? -1 : 1;
+            // so the first key block of each workgroup walks down from it; the
+            // second block of a causal pair walks up from its diagonal tile: a
+            // workgroup starts it after the tiles of its first block, and the first
+            // range is shorter by as many tiles as the second starts higher, so at
+            // each step every workgroup in its second pass is on the same tile too.
+            // Without causal mask every range starts at tile 0, so all walk up from
+            // it; under causal + window the ranges have the same length nq and
+            // different starts, so each walks up from the tile whose index is a
+            // multiple of nq, wrapping to its first tile (at step s every workgroup
+            // is on a tile congruent to s mod nq).
+            const int tdir = a.causal && !a.window && !pass ? -1 : 1;
             const int trot = a.causal && a.window && nq > 0 ? (nq - qt_lo % nq) % nq : 0;
             auto tile_of = [&](int st) {  // query tile at position st of the walk
                 int u = st + trot;
