@@ -304,6 +304,10 @@ template <class T, int DMAX, int BKV, int RW, int DW, int NS> struct Fwd2Cfg {
     static constexpr int NW = RW * DW, NT = 64 * NW, BQ = 32 * RW;
     static constexpr int DS = DMAX / DW, SCH = DS / 8, NKG = SCH / 2, NDB = DS / 32;
     static constexpr int NKB = BKV / 32, NPG = BKV / 16;
+    // K fragments in flight per batch of score MFMAs. A 256-wide d slice keeps
+    // 64 registers of Q fragments and 128 of O accumulators per wave, which at
+    // two waves per SIMD leaves room for one fragment ahead of its MFMA.
+    static constexpr int FB = DS >= 256 ? 1 : NKG < 8 ? NKG : 8;
     static constexpr int ROWB = tile_row_bytes(DMAX), TILEB = BKV * ROWB, STAGEB = 2 * TILEB;
     static constexpr int RED = DW > 1 ? RW * DW * NKB * 16 * 64 * 4 : 0;
     static constexpr int LDS = NS * STAGEB + RED;
@@ -404,7 +408,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
             // requested before the previous batch's MFMAs
             f32x16 s[C::NKB];
             {
-                constexpr int FB = C::NKG < 8 ? C::NKG : 8, BPK = C::NKG / FB, NB = C::NKB * BPK;
+                constexpr int FB = C::FB, BPK = C::NKG / FB, NB = C::NKB * BPK;
                 auto load = [&](int k, u32x4 (&f)[FB]) {
 #pragma unroll
                     for (int i = 0; i < FB; ++i) f[i] = ld16(kl + to.natural(32 * (k / BPK), (k % BPK) * FB + i, cb));
@@ -1662,7 +1666,7 @@ inline int dmax16(int D) {
 #define FA2_FWD_128 64, 4, 1, 2, 2
 #endif
 #ifndef FA2_FWD_256
-#define FA2_FWD_256 32, 2, 2, 2, 2
+#define FA2_FWD_256 32, 4, 1, 2, 2
 #endif
 #ifndef FA2_FWD_512
 #define FA2_FWD_512 32, 1, 4, 1, 2
