@@ -1387,10 +1387,10 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
                     const char* tb = smem + slot * C::STAGEB + toff;  // dO of tile it
                     const char* sn = smem + nslot * C::STAGEB;        // tile it+1
                     const char* pcur = pbase + (it & 1) * C::PBUF;    // P of tile it
-                    wait_vm<0>();   // this wave's share of tile it+1
-                    lds_barrier();  // P of tile it visible; tile it+1 visible; tile it-1 done
+                    px = ld16(pcur);  // this wave's own P: read before the barrier, no wait after it
+                    wait_vm<0>();     // this wave's share of tile it+1
+                    lds_barrier();    // P of tile it visible; tile it+1 visible; tile it-1 done
                     if (it + 2 < n_it) issue();
-                    px = ld16(pcur);
                     const int q0 = tile_of(sa) * BQ, hq = g * reps + ha;
 #pragma unroll
                     for (int gi = 0; gi < C::NKG; ++gi) fr0[gi] = ld16(sn + aoff + to.natural(0, gi, cb));
@@ -1529,8 +1529,13 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
                 // MFMAs; dS = P (dP - Delta) is formed one row group ahead.
                 const int nslot = slot == C::NS - 1 ? 0 : slot + 1;
                 PF<T> pf[C::NPG];
+                // P of every row group requested at once, right after the barrier
+                // that publishes it (one LDS wait instead of one per row group)
+                u32x4 pp[C::NPG];
+#pragma unroll
+                for (int gg = 0; gg < C::NPG; ++gg) pp[gg] = ld16(pb + gg * 1024);
                 auto ds_group = [&](int gg) {
-                    const T8 pv = __builtin_bit_cast(T8, ld16(pb + gg * 1024));
+                    const T8 pv = __builtin_bit_cast(T8, pp[gg]);
                     const int rb = gg >> 1, hf = gg & 1;
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
