@@ -1161,9 +1161,16 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
 
     TileOffs<C::ROWB> to;
     to.init(lane);
-    DmaPlan<BQ, DMAX, C::NW> dma;
-    dma.init(lane, w, D);
-    constexpr int WD = KW;  // delta is fetched by the first dK wave, lse by wave 0
+    // Who streams the Q/dO tiles. A wave stalls while the CU's memory pipeline
+    // takes its LDS-DMA requests, and every wave requests its pieces right after
+    // the barrier. At two waves per SIMD the dV waves, which otherwise wait at
+    // the next barrier, issue all of them and the dK waves none (D = 128: 0.273
+    // -> 0.268 ms on the 2048-token workload); with one wave per SIMD (D = 256)
+    // every wave issues its share (0.344 against 0.358 ms the other way).
+    constexpr bool DMA_V = OCC >= 2;
+    DmaPlan<BQ, DMAX, (DMA_V ? KW : C::NW)> dma;
+    dma.init(lane, DMA_V ? w % KW : w, D);
+    constexpr int WD = DMA_V ? 1 : KW;  // lse is fetched by wave 0, delta by wave WD
     char* const pbase = smem + C::NS * C::STAGEB + (kw * C::NPG * 64 + lane) * 16;
     constexpr int cb = 0;  // chunk base of the tile columns (the head dim is not split)
     const int aoff = vw ? 0 : C::TILEB;  // phase-A operand: Q (dV wave) or dO (dK wave)
@@ -1227,15 +1234,17 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
                 const dsc_t rdo = make_dsc(reinterpret_cast<const T*>(a.dO) + qrow0 * Dv, obytes);
                 char* st = smem + slot_issue * C::STAGEB;
                 const int qrow = tile_of(st_issue) * BQ;
-                dma.issue(rq, lds_of(st, smem), qrow, D, w);
-                if (Dv == D) dma.issue(rdo, lds_of(st + C::TILEB, smem), qrow, D, w);
-                else dma.issue_pitch(rdo, lds_of(st + C::TILEB, smem), qrow, Dv, w, lane);
+                if constexpr (!DMA_V || V) {
+                    dma.issue(rq, lds_of(st, smem), qrow, D, w);
+                    if (Dv == D) dma.issue(rdo, lds_of(st + C::TILEB, smem), qrow, D, w);
+                    else dma.issue_pitch(rdo, lds_of(st + C::TILEB, smem), qrow, Dv, w, lane);
+                }
                 const size_t lhead = (size_t)(b * a.Hq + hq_issue) * a.Lq;
-                if (w == 0) {
+                if ((!DMA_V || V) && w == 0) {
                     const dsc_t rl = make_dsc(a.lse + lhead, (uint32_t)a.Lq * 4u);
                     if (lane < BQ) dma4(rl, lds_of(st + 2 * C::TILEB, smem), (uint32_t)(qrow + lane) * 4u);
                 }
-                if (w == WD) {
+                if ((!DMA_V || V) && w == WD) {
                     const dsc_t rd = make_dsc(a.delta + lhead, (uint32_t)a.Lq * 4u);
                     if (lane < BQ) dma4(rd, lds_of(st + 2 * C::TILEB + BQ * 4, smem), (uint32_t)(qrow + lane) * 4u);
                 }
