@@ -298,6 +298,70 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 
 // ===========================================================================
+// Output tiles through LDS
+// ===========================================================================
+// A wave's 32-row output tile is held as transposed MFMA accumulators: element
+// 4qd + j of acc[db] in lane (h, n) is row n, column 32db + 8qd + 4h + j.
+// Stored directly, every instruction writes 8 bytes into each of 32 rows
+// (sixteen 16-byte pieces per row and instruction group); the epilogue of the
+// forward spent about 4500 cycles per wave in such stores. store_rows passes
+// the tile through the wave's LDS region instead (rows of COLS values,
+// 16-byte chunks XOR-swizzled by row) and stores whole row pieces: RPI rows
+// of COLS columns per instruction, in passes of COLS columns.
+template <int DMAX> struct RowStore {
+    static constexpr int COLS = DMAX >= 96 ? 128 : DMAX;  // columns per pass
+    static constexpr int NCH = COLS / 8;                  // 16-byte chunks per row
+    static constexpr int RPI = 64 / NCH;                  // rows per store instruction
+    static constexpr int ROWB = 2 * COLS;                 // LDS bytes per row
+    static constexpr int BYTES = 32 * ROWB;               // LDS bytes per wave
+    static constexpr int NDB = DMAX / 32, DBP = COLS / 32, NP = (NDB + DBP - 1) / DBP;
+};
+template <class T> __device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d);
+template <> __device__ __forceinline__ u32x2 pack4<__bf16>(float a, float b, float c, float d) {
+    return __builtin_bit_cast(u32x2, bf16x4{(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d});
+}
+template <> __device__ __forceinline__ u32x2 pack4<_Float16>(float a, float b, float c, float d) {
+    return __builtin_bit_cast(u32x2, f16x4{(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d});
+}
+// Rows [0, nrows) and columns [0, ncols) of the tile, each value times `mul`
+// (the lane's row factor), to base + r * pitch + col. `ws`: this wave's
+// RowStore<DMAX>::BYTES of LDS, used by no other wave meanwhile.
+template <class T, int DMAX>
+__device__ __forceinline__ void store_rows(char* ws, const f32x16 (&acc)[DMAX / 32], float mul, T* base, size_t pitch,
+                                           int nrows, int ncols, int lane) {
+    using R = RowStore<DMAX>;
+    // the lane index made opaque here, so that the address arithmetic below
+    // is done at the store and not hoisted ahead of the tile loop into
+    // registers that the loop needs
+    asm volatile("" : "+v"(lane));
+    const int h = lane >> 5, ln = lane & 31;
+    const int c = lane % R::NCH, r0 = lane / R::NCH;
+#pragma unroll
+    for (int p = 0; p < R::NP; ++p) {
+#pragma unroll
+        for (int b4 = 0; b4 < R::DBP; ++b4) {
+            const int db = p * R::DBP + b4;
+            if (db < R::NDB) {
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd) {
+                    const int cw = 4 * b4 + qd;  // chunk of this lane's 4 values, half h
+                    st8(ws + ln * R::ROWB + ((cw ^ (ln & (R::NCH - 1))) << 4) + 8 * h,
+                        pack4<T>(acc[db][4 * qd] * mul, acc[db][4 * qd + 1] * mul, acc[db][4 * qd + 2] * mul,
+                                 acc[db][4 * qd + 3] * mul));
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 32 / R::RPI; ++i) {
+            const int r = i * R::RPI + r0;
+            const u32x4 v = ld16(ws + r * R::ROWB + ((c ^ (r & (R::NCH - 1))) << 4));
+            const int col = p * R::COLS + 8 * c;
+            if (r < nrows && col < ncols) st16(base + (size_t)r * pitch + col, v);
+        }
+    }
+}
+
+// ===========================================================================
 // Forward
 // ===========================================================================
 template <class T, int DMAX, int BKV, int RW, int DW, int NS> struct Fwd2Cfg {
@@ -535,7 +599,22 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_fwd_lds_kernel(FwdArgs a
     for (int t = 0; t < n_t; t += NS) unroll_slots<0, NS>(t, n_t, step);
 
     const float l = sum_halves(l_run);
-    if (row < a.Lq) {
+    // At D = 256 O goes through the stage that holds neither the last tile nor
+    // a pending DMA (every wave is done with tile n_t - 2 since the last
+    // barrier): 0.152 -> 0.145 ms on the 8192-token windowed workload. At
+    // D <= 128 the same measured 0.1554 -> 0.1561 ms on the 2048-token
+    // workload and 10.87 -> 11.31 ms at 32768 tokens, so there the lanes
+    // store their own pieces.
+    if constexpr (DW == 1 && DMAX >= 256) {
+        static_assert(C::NW * RowStore<DMAX>::BYTES <= C::STAGEB, "output staging does not fit in a stage");
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        char* ws = smem + ((n_t + NS - 2) % NS) * C::STAGEB + w * RowStore<DMAX>::BYTES;
+        const int r0 = i0 + 32 * rw;
+        T* ob = reinterpret_cast<T*>(a.o) + ((size_t)(b * a.Hq + hq) * a.Lq + r0) * Dv;
+        store_rows<T, DMAX>(ws, o, inv, ob, (size_t)Dv, a.Lq - r0, Dv, lane);
+        if (row < a.Lq && h == 0)
+            a.lse[(size_t)(b * a.Hq + hq) * a.Lq + row] = l > 0.f ? (m_ref + fast_log2(l)) * kLn2 : -INFINITY;
+    } else if (row < a.Lq) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
         T* op = reinterpret_cast<T*>(a.o) + ((size_t)(b * a.Hq + hq) * a.Lq + row) * Dv;
 #pragma unroll
@@ -845,7 +924,16 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
         prio_valu();
     }
 
-    if (row < a.Lq) {
+    if constexpr (DW == 1) {
+        // dQ through the stage that holds neither the last tile nor a pending DMA
+        // (0.1943 -> 0.1894 ms on the 2048-token workload, 0.2426 -> 0.2337 ms
+        // on the 8192-token windowed one at D = 256)
+        static_assert(C::NW * RowStore<DMAX>::BYTES <= C::STAGEB, "output staging does not fit in a stage");
+        char* ws = smem + ((n_t + NS - 2) % NS) * C::STAGEB + w * RowStore<DMAX>::BYTES;
+        const int r0 = i0 + 32 * rw;
+        T* ob = reinterpret_cast<T*>(a.dq) + qhead + (size_t)r0 * D;
+        store_rows<T, DMAX>(ws, acc, a.scale, ob, (size_t)D, a.Lq - r0, D, lane);
+    } else if (row < a.Lq) {
         T* op = reinterpret_cast<T*>(a.dq) + qhead + (size_t)row * D;
         const float sc = a.scale;
 #pragma unroll
@@ -1580,6 +1668,10 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
             }
             }
 
+            // dK or dV of the wave's 32 keys through a stage that holds neither
+            // the last tile nor a pending DMA (every wave is done with the tiles
+            // before the last since the last barrier): waves 0-3 use stage
+            // (n_it + 1) % 3, waves 4-7 stage (n_it + 2) % 3
             if (key < a.Lkv) {
                 T* op = reinterpret_cast<T*>(V ? a.dv : a.dk) + (V ? kvhead_v : kvhead) + (size_t)key * Do;
                 const float sc = V ? 1.f : a.scale;
