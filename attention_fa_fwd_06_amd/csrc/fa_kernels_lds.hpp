@@ -1211,7 +1211,7 @@ template <class T, int DMAX, int BQ, int KW> struct DkvPipeCfg {
     static constexpr int PBUF = KW * NPG * 64 * 16;  // P of every key block as MFMA operands, lane-major
     static constexpr int LDS = NS * STAGEB + 2 * PBUF;
     static_assert(LDS <= kLdsBudget, "dK/dV stages do not fit in LDS");
-    static_assert(DMAX % 32 == 0 && (BQ == 32 || BQ == 64), "configuration");
+    static_assert(DMAX % 32 == 0 && (BQ == 32 || BQ == 64) && KW >= 2, "configuration");
 };
 
 template <class T, int DMAX, int BQ, int KW, int OCC, int PRIO, bool MASK>
@@ -1250,15 +1250,17 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
     TileOffs<C::ROWB> to;
     to.init(lane);
     // Who streams the Q/dO tiles. A wave stalls while the CU's memory pipeline
-    // takes its LDS-DMA requests, and every wave requests its pieces right after
-    // the barrier. At two waves per SIMD the dV waves, which otherwise wait at
-    // the next barrier, issue all of them and the dK waves none (D = 128: 0.273
-    // -> 0.268 ms on the 2048-token workload); with one wave per SIMD (D = 256)
-    // every wave issues its share (0.344 against 0.358 ms the other way).
-    constexpr bool DMA_V = OCC >= 2;
-    DmaPlan<BQ, DMAX, (DMA_V ? KW : C::NW)> dma;
-    dma.init(lane, DMA_V ? w % KW : w, D);
-    constexpr int WD = DMA_V ? 1 : KW;  // lse is fetched by wave 0, delta by wave WD
+    // takes its LDS-DMA requests, and the requests go out right after the
+    // barrier, so they are left to the waves that otherwise wait at the next
+    // one: at two waves per SIMD (D <= 128) the dV waves issue all of them
+    // (0.273 -> 0.268 ms on the 2048-token workload), at one wave per SIMD
+    // (D = 256) the dK waves (0.349 -> 0.331 ms on the 8192-token windowed
+    // workload; the dV waves there: 0.358 ms).
+    constexpr bool DMA_V = OCC >= 2;   // the dV waves issue the DMA, else the dK waves
+    DmaPlan<BQ, DMAX, KW> dma;
+    const int wdma = DMA_V ? w : w - KW;  // index among the issuing waves (negative: none)
+    dma.init(lane, wdma < 0 || wdma >= KW ? 0 : wdma, D);
+    constexpr int WL = DMA_V ? 0 : KW;      // lse is fetched by wave WL, delta by wave WL + 1
     char* const pbase = smem + C::NS * C::STAGEB + (kw * C::NPG * 64 + lane) * 16;
     constexpr int cb = 0;  // chunk base of the tile columns (the head dim is not split)
     const int aoff = vw ? 0 : C::TILEB;  // phase-A operand: Q (dV wave) or dO (dK wave)
@@ -1322,17 +1324,17 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
                 const dsc_t rdo = make_dsc(reinterpret_cast<const T*>(a.dO) + qrow0 * Dv, obytes);
                 char* st = smem + slot_issue * C::STAGEB;
                 const int qrow = tile_of(st_issue) * BQ;
-                if constexpr (!DMA_V || V) {
-                    dma.issue(rq, lds_of(st, smem), qrow, D, w);
-                    if (Dv == D) dma.issue(rdo, lds_of(st + C::TILEB, smem), qrow, D, w);
-                    else dma.issue_pitch(rdo, lds_of(st + C::TILEB, smem), qrow, Dv, w, lane);
+                if constexpr (DMA_V == V) {
+                    dma.issue(rq, lds_of(st, smem), qrow, D, wdma);
+                    if (Dv == D) dma.issue(rdo, lds_of(st + C::TILEB, smem), qrow, D, wdma);
+                    else dma.issue_pitch(rdo, lds_of(st + C::TILEB, smem), qrow, Dv, wdma, lane);
                 }
                 const size_t lhead = (size_t)(b * a.Hq + hq_issue) * a.Lq;
-                if ((!DMA_V || V) && w == 0) {
+                if (DMA_V == V && w == WL) {
                     const dsc_t rl = make_dsc(a.lse + lhead, (uint32_t)a.Lq * 4u);
                     if (lane < BQ) dma4(rl, lds_of(st + 2 * C::TILEB, smem), (uint32_t)(qrow + lane) * 4u);
                 }
-                if ((!DMA_V || V) && w == WD) {
+                if (DMA_V == V && w == WL + 1) {
                     const dsc_t rd = make_dsc(a.delta + lhead, (uint32_t)a.Lq * 4u);
                     if (lane < BQ) dma4(rd, lds_of(st + 2 * C::TILEB + BQ * 4, smem), (uint32_t)(qrow + lane) * 4u);
                 }
