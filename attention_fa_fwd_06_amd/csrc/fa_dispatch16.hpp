@@ -5,6 +5,7 @@
 #pragma once
 
 #include "fa_kernels_short.hpp"
+#include "fa_kernels_dkvq.hpp"
 
 namespace fa {
 namespace lds {
@@ -53,7 +54,7 @@ template <class T> hipError_t launch_dkv16(const BwdArgs& a, hipStream_t s) {
         case 64: return launch_dkv_pipe<T, 64, FA2_DKVS_64>(a, s);
         case 96: return launch_dkv_pipe<T, 96, FA2_DKVS_96>(a, s);
         case 128: return launch_dkv_pipe<T, 128, FA2_DKVS_128>(a, s);
-        case 256: return launch_dkv_pipe<T, 256, FA2_DKVS_256>(a, s);
+        case 256: return launch_dkv_quad<T, 256, 32>(a, s);
         default: return launch_dkv2<T, 512, FA2_DKV_512>(a, s);
     }
 }

@@ -1251,16 +1251,10 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
     to.init(lane);
     // Who streams the Q/dO tiles. A wave stalls while the CU's memory pipeline
     // takes its LDS-DMA requests, and the requests go out right after the
-    // barrier, so they are left to the waves that otherwise wait at the next
-    // one: at two waves per SIMD (D <= 128) the dV waves issue all of them
-    // (0.273 -> 0.268 ms on the 2048-token workload), at one wave per SIMD
-    // (D = 256) the dK waves (0.349 -> 0.331 ms on the 8192-token windowed
-    // workload; the dV waves there: 0.358 ms).
-    constexpr bool DMA_V = OCC >= 2;   // the dV waves issue the DMA, else the dK waves
+    // barrier, so they are left to the dV waves, which otherwise wait at the
+    // next one (0.273 -> 0.268 ms on the 2048-token workload).
     DmaPlan<BQ, DMAX, KW> dma;
-    const int wdma = DMA_V ? w : w - KW;  // index among the issuing waves (negative: none)
-    dma.init(lane, wdma < 0 || wdma >= KW ? 0 : wdma, D);
-    constexpr int WL = DMA_V ? 0 : KW;      // lse is fetched by wave WL, delta by wave WL + 1
+    dma.init(lane, vw ? w : 0, D);
     char* const pbase = smem + C::NS * C::STAGEB + (kw * C::NPG * 64 + lane) * 16;
     constexpr int cb = 0;  // chunk base of the tile columns (the head dim is not split)
     const int aoff = vw ? 0 : C::TILEB;  // phase-A operand: Q (dV wave) or dO (dK wave)
@@ -1324,17 +1318,17 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
                 const dsc_t rdo = make_dsc(reinterpret_cast<const T*>(a.dO) + qrow0 * Dv, obytes);
                 char* st = smem + slot_issue * C::STAGEB;
                 const int qrow = tile_of(st_issue) * BQ;
-                if constexpr (DMA_V == V) {
-                    dma.issue(rq, lds_of(st, smem), qrow, D, wdma);
-                    if (Dv == D) dma.issue(rdo, lds_of(st + C::TILEB, smem), qrow, D, wdma);
-                    else dma.issue_pitch(rdo, lds_of(st + C::TILEB, smem), qrow, Dv, wdma, lane);
+                if constexpr (V) {
+                    dma.issue(rq, lds_of(st, smem), qrow, D, w);
+                    if (Dv == D) dma.issue(rdo, lds_of(st + C::TILEB, smem), qrow, D, w);
+                    else dma.issue_pitch(rdo, lds_of(st + C::TILEB, smem), qrow, Dv, w, lane);
                 }
                 const size_t lhead = (size_t)(b * a.Hq + hq_issue) * a.Lq;
-                if (DMA_V == V && w == WL) {
+                if (V && w == 0) {
                     const dsc_t rl = make_dsc(a.lse + lhead, (uint32_t)a.Lq * 4u);
                     if (lane < BQ) dma4(rl, lds_of(st + 2 * C::TILEB, smem), (uint32_t)(qrow + lane) * 4u);
                 }
-                if (DMA_V == V && w == WL + 1) {
+                if (V && w == 1) {
                     const dsc_t rd = make_dsc(a.delta + lhead, (uint32_t)a.Lq * 4u);
                     if (lane < BQ) dma4(rd, lds_of(st + 2 * C::TILEB + BQ * 4, smem), (uint32_t)(qrow + lane) * 4u);
                 }
@@ -1801,8 +1795,8 @@ inline int dmax16(int D) {
 #define FA2_DKV_512 32, 1, 4, 1, 2
 #endif
 
-// dK/dV on wave pairs: <query tile, key blocks of 32, min waves per SIMD, dV-wave priority>. At D = 256 (one wave per SIMD) the raised priority measured
-// 0.3375 against 0.3351 ms without it on the windowed 8192-token workload.
+// dK/dV on wave pairs (head dims up to 128): <query tile, key blocks of 32, min
+// waves per SIMD, dV-wave priority>.
 #ifndef FA2_DKVS_32
 #define FA2_DKVS_32 64, 4, 2, 1
 #endif
@@ -1814,9 +1808,6 @@ inline int dmax16(int D) {
 #endif
 #ifndef FA2_DKVS_128
 #define FA2_DKVS_128 64, 4, 2, 1
-#endif
-#ifndef FA2_DKVS_256
-#define FA2_DKVS_256 32, 2, 1, 0
 #endif
 
 }  // namespace lds
