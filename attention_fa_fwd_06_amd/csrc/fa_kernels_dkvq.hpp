@@ -12,9 +12,13 @@
 //   C: dP = dO V^T and dS = P (dP - Delta), stored for D
 //   D: dK += Q^T dS, from C's dS
 // A and C keep the K or V fragments and no accumulator, B and D an
-// accumulator and no fragments, so two waves share each SIMD: A with B and
-// C with D (waves w and w + 4), 32 MFMAs of each 32-row tile on every SIMD.
-// A workgroup owns two key blocks (eight waves, 64 keys).
+// accumulator and no fragments, so two waves share each SIMD, 32 MFMAs of
+// each 32-row tile on every SIMD. A workgroup owns two key blocks (eight
+// waves, 64 keys). The two producers of a key block share a SIMD, and so do
+// its two consumers: A's iteration is MFMAs then exponentials and C's is
+// dS arithmetic then MFMAs, so each covers the other's VALU phase, while
+// the consumers are MFMA streams alone. (A with B and C with D on a SIMD:
+// 287.4 against 275.1 us on the 8192-token windowed workload.)
 //
 // One barrier per element of the walk over (query tile, head). In iteration t
 // (after barrier t) A computes S and P of element t+1; B updates dV with P of
@@ -74,9 +78,12 @@ __global__ __launch_bounds__(512, 2) void fa_dkv_quad_kernel(BwdArgs a, int pair
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: descriptors and roles depend on it
     const int h = lane >> 5, ln = lane & 31;
-    // role 0..3 = A, B, C, D (see above); waves w and w + 4 share a SIMD
-    const int role = (w < 4 ? 0 : 1) + ((w & 1) ? 2 : 0);
+    // role 0..3 = A, B, C, D (see above); waves w and w + 4 share a SIMD:
+    // A and C of key block kb on SIMD 2 kb, its B and D on SIMD 2 kb + 1
+    const int role = ((w & 1) ? 1 : 0) + (w >= 4 ? 2 : 0);
     const int kb = (w >> 1) & 1;
+    const int cidx = w >> 1;  // index of a consumer (B, D) among the four
+    const int wl = 1, wd = 3;  // the consumers that fetch lse and delta
 
     const int nkt = (a.Lkv + C::BKV - 1) / C::BKV;
     const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -99,7 +106,7 @@ __global__ __launch_bounds__(512, 2) void fa_dkv_quad_kernel(BwdArgs a, int pair
     TileOffs<C::ROWB> to;
     to.init(lane);
     DmaPlan<BQ, DMAX, 4> dma;  // B and D waves (w = 4..7) issue
-    dma.init(lane, w >= 4 ? w - 4 : 0, D);
+    dma.init(lane, (role == 1 || role == 3) ? cidx : 0, D);
     char* const pbuf = smem + C::NS * C::STAGEB;              // P of elements with parity 0, 1
     char* const sbuf = pbuf + 2 * C::OPB;                      // dS of elements with parity 0, 1
     const int lofs = (kb * C::NPG * 64 + lane) * 16;           // this lane's piece of a key block's operand
@@ -157,14 +164,14 @@ __global__ __launch_bounds__(512, 2) void fa_dkv_quad_kernel(BwdArgs a, int pair
                     char* st = stage(e);
                     const dsc_t rq = make_dsc(reinterpret_cast<const T*>(a.q) + qrow0 * D, qbytes);
                     const dsc_t rdo = make_dsc(reinterpret_cast<const T*>(a.dO) + qrow0 * Dv, obytes);
-                    dma.issue(rq, lds_of(st, smem), qrow, D, w - 4);
-                    if (Dv == D) dma.issue(rdo, lds_of(st + C::TILEB, smem), qrow, D, w - 4);
-                    else DmaPlan<BQ, DMAX, 4>::issue_pitch(rdo, lds_of(st + C::TILEB, smem), qrow, Dv, w - 4, lane);
-                    if (w == 4) {
+                    dma.issue(rq, lds_of(st, smem), qrow, D, cidx);
+                    if (Dv == D) dma.issue(rdo, lds_of(st + C::TILEB, smem), qrow, D, cidx);
+                    else DmaPlan<BQ, DMAX, 4>::issue_pitch(rdo, lds_of(st + C::TILEB, smem), qrow, Dv, cidx, lane);
+                    if (w == wl) {
                         const dsc_t rl = make_dsc(a.lse + qrow0, (uint32_t)a.Lq * 4u);
                         if (lane < BQ) dma4(rl, lds_of(st + 2 * C::TILEB, smem), (uint32_t)(qrow + lane) * 4u);
                     }
-                    if (w == 5) {
+                    if (w == wd) {
                         const dsc_t rd = make_dsc(a.delta + qrow0, (uint32_t)a.Lq * 4u);
                         if (lane < BQ) dma4(rd, lds_of(st + 2 * C::TILEB + BQ * 4, smem), (uint32_t)(qrow + lane) * 4u);
                     }
