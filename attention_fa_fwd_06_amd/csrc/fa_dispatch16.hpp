@@ -6,6 +6,7 @@
 
 #include "fa_kernels_short.hpp"
 #include "fa_kernels_dkvq.hpp"
+#include "fa_kernels_dq3.hpp"
 
 namespace fa {
 namespace lds {
@@ -40,7 +41,7 @@ template <class T> hipError_t launch_dq16(const BwdArgs& a, hipStream_t s) {
         case 64: return launch_dq2<T, 64, FA2_DQ_64>(a, s);
         case 96: return launch_dq2<T, 96, FA2_DQ_96>(a, s);
         case 128: return launch_dq2<T, 128, FA2_DQ_128>(a, s);
-        case 256: return launch_dq2<T, 256, FA2_DQ_256>(a, s);
+        case 256: return launch_dq_tri<T, 256>(a, s);
         default: return launch_dq2<T, 512, FA2_DQ_512>(a, s);
     }
 }

@@ -926,8 +926,7 @@ __global__ __launch_bounds__(64 * RW * DW, OCC) void fa_dq_lds_kernel(BwdArgs a)
 
     if constexpr (DW == 1) {
         // dQ through the stage that holds neither the last tile nor a pending DMA
-        // (0.1943 -> 0.1894 ms on the 2048-token workload, 0.2426 -> 0.2337 ms
-        // on the 8192-token windowed one at D = 256)
+        // (0.1943 -> 0.1894 ms on the 2048-token workload)
         static_assert(C::NW * RowStore<DMAX>::BYTES <= C::STAGEB, "output staging does not fit in a stage");
         char* ws = smem + ((n_t + NS - 2) % NS) * C::STAGEB + w * RowStore<DMAX>::BYTES;
         const int r0 = i0 + 32 * rw;
@@ -1784,9 +1783,6 @@ inline int dmax16(int D) {
 #endif
 #ifndef FA2_DQ_128
 #define FA2_DQ_128 64, 4, 1, 2, 2
-#endif
-#ifndef FA2_DQ_256
-#define FA2_DQ_256 64, 4, 1, 1, 2
 #endif
 #ifndef FA2_DQ_512
 #define FA2_DQ_512 32, 1, 4, 1, 2
