@@ -22,8 +22,10 @@
 // iteration before) and A's P of t, stores it and computes dP of t+1; D
 // updates dQ with the dS of t-1 stored the iteration before. K goes through
 // a four-slot ring (t-1 for D, t, t+1 for A, t+2 in flight), V through two
-// (t+1 for C, t+2 in flight); P and dS have two buffers each. The D waves,
-// whose MFMA chains wait on the producers', issue the LDS-DMA requests.
+// (t+1 for C, t+2 in flight); P and dS have two buffers each. The C waves
+// issue the LDS-DMA requests (by the D waves: 219.3 against 216.0 us on the
+// 8192-token windowed workload; by the A waves 225.2), and every chain
+// requests its LDS fragments three MFMAs ahead (two: 220.2 against 217.5).
 // dQ leaves through LDS (whole row pieces per store instruction): the V
 // ring and the two K slots that no wave reads after the last barrier.
 #pragma once
@@ -101,15 +103,14 @@ __global__ __launch_bounds__(1024, 4) void fa_dq_tri_kernel(BwdArgs a) {
         constexpr int R = decltype(rl)::value;
         constexpr bool RA = R == 0, RC = R == 1, RD = R >= 2;
         constexpr int DB0 = RD ? (R - 2) * C::NHB : 0;  // D: first column block of its half
-        const int wdma = (R - 2) * 4 + (w & 3);         // D: index among the eight issuing waves
         TileOffs<C::ROWB> to;  // set up per role, so that each keeps only what it uses
         to.init(lane);
-        auto issue = [&](int t) {  // D waves: K and V of tile t (offsets recomputed, no registers held)
-            if constexpr (RD) {
-                using P = DmaPlan<C::BKV, DMAX, 2 * C::RB>;
+        auto issue = [&](int t) {  // C waves: K and V of tile t (offsets recomputed, no registers held)
+            if constexpr (RC) {
+                using P = DmaPlan<C::BKV, DMAX, C::RB>;
                 const int j = (t_lo + t) * C::BKV;
-                P::issue_pitch(rk, lds_of(kslot(t), smem), j, D, wdma, lane);
-                P::issue_pitch(rv, lds_of(vslot(t), smem), j, Dv, wdma, lane);
+                P::issue_pitch(rk, lds_of(kslot(t), smem), j, D, w & 3, lane);
+                P::issue_pitch(rv, lds_of(vslot(t), smem), j, Dv, w & 3, lane);
             }
         };
         // register operand of the row: Q^T (A) or dO^T (C) fragments
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(1024, 4) void fa_dq_tri_kernel(BwdArgs a) {
         // x = (natural fragments of the tile at `op`) x rf over the head dim
         auto chain = [&](const char* op, f32x16& x) {
             x = zero16();
-            lookahead<C::NKG, 2>([&](int n) { return ld16(op + to.natural(0, n, cb)); },
+            lookahead<C::NKG, 3>([&](int n) { return ld16(op + to.natural(0, n, cb)); },
                                  [&](int n, const u32x4& f) {
                                      Mma<T>::nat(x, f, rf[n < (int)(sizeof(rf) / sizeof(rf[0])) ? n : 0]);
                                  });
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(1024, 4) void fa_dq_tri_kernel(BwdArgs a) {
                     const char* kl = kslot(t - 1);
                     // dQ^T[:, DB0 + i] += K^T (column block DB0 + i, key group gg) x dS^T
                     // of group gg
-                    lookahead<C::NPG * C::NHB, 2>(
+                    lookahead<C::NPG * C::NHB, 3>(
                         [&](int n) {
                             const int gg = n / C::NHB, db = DB0 + n % C::NHB;
                             return rd_tr(kl + to.transposed(gg, db, cb, 0), kl + to.transposed(gg, db, cb, 1));
