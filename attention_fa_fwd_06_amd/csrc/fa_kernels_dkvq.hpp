@@ -26,7 +26,9 @@
 // of t, stores it and computes dP of t+1; D updates dK with the dS of t-1
 // stored the iteration before. Four stages: t-1 (D), t, t+1 and t+2 in
 // flight; P and dS have two buffers each. The consumers, whose MFMA chains
-// wait on the producers', issue the LDS-DMA requests.
+// wait on the producers', issue the LDS-DMA requests (275.9 us on the
+// 8192-token windowed workload; the producers 306.0, the dS waves alone
+// 292.5).
 #pragma once
 
 #include "fa_kernels_lds.hpp"
@@ -105,7 +107,7 @@ __global__ __launch_bounds__(512, 2) void fa_dkv_quad_kernel(BwdArgs a, int pair
 
     TileOffs<C::ROWB> to;
     to.init(lane);
-    DmaPlan<BQ, DMAX, 4> dma;  // B and D waves (w = 4..7) issue
+    DmaPlan<BQ, DMAX, 4> dma;  // the B and D waves (odd w) issue
     dma.init(lane, (role == 1 || role == 3) ? cidx : 0, D);
     char* const pbuf = smem + C::NS * C::STAGEB;              // P of elements with parity 0, 1
     char* const sbuf = pbuf + 2 * C::OPB;                      // dS of elements with parity 0, 1
