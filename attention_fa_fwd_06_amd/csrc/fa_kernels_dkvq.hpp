@@ -25,10 +25,13 @@
 // t; C forms dS of t from its dP of t (computed the iteration before) and P
 // of t, stores it and computes dP of t+1; D updates dK with the dS of t-1
 // stored the iteration before. Four stages: t-1 (D), t, t+1 and t+2 in
-// flight; P and dS have two buffers each. The consumers, whose MFMA chains
-// wait on the producers', issue the LDS-DMA requests (275.9 us on the
-// 8192-token windowed workload; the producers 306.0, the dS waves alone
-// 292.5).
+// flight; P and dS have two buffers each. The dV consumers (B) issue all the
+// LDS-DMA requests right after the barrier. A wave stalls while the CU takes
+// its requests; with B and D sharing them, D (the longest chain) spent about
+// half of each iteration there. 8192-token windowed workload, each line one
+// box: B alone 277.8 us, B and D 283.2, B and D with B's share issued after
+// its products 278.8; B and D 278.4, with D's share after its products 304.1;
+// B and D 275.9, the producers 306.0, C alone 292.5.
 #pragma once
 
 #include "fa_kernels_lds.hpp"
@@ -84,8 +87,8 @@ __global__ __launch_bounds__(512, 2) void fa_dkv_quad_kernel(BwdArgs a, int pair
     // A and C of key block kb on SIMD 2 kb, its B and D on SIMD 2 kb + 1
     const int role = ((w & 1) ? 1 : 0) + (w >= 4 ? 2 : 0);
     const int kb = (w >> 1) & 1;
-    const int cidx = w >> 1;  // index of a consumer (B, D) among the four
-    const int wl = 1, wd = 3;  // the consumers that fetch lse and delta
+    const int cidx = w >> 1;  // B waves (w = 1, 3): index among the two that issue the DMA
+    const int wl = 1, wd = 3;  // the B waves that fetch lse and delta
 
     const int nkt = (a.Lkv + C::BKV - 1) / C::BKV;
     const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -107,8 +110,8 @@ __global__ __launch_bounds__(512, 2) void fa_dkv_quad_kernel(BwdArgs a, int pair
 
     TileOffs<C::ROWB> to;
     to.init(lane);
-    DmaPlan<BQ, DMAX, 4> dma;  // the B and D waves (odd w) issue
-    dma.init(lane, (role == 1 || role == 3) ? cidx : 0, D);
+    DmaPlan<BQ, DMAX, 2> dma;
+    dma.init(lane, role == 1 ? cidx : 0, D);
     char* const pbuf = smem + C::NS * C::STAGEB;              // P of elements with parity 0, 1
     char* const sbuf = pbuf + 2 * C::OPB;                      // dS of elements with parity 0, 1
     const int lofs = (kb * C::NPG * 64 + lane) * 16;           // this lane's piece of a key block's operand
@@ -159,8 +162,8 @@ __global__ __launch_bounds__(512, 2) void fa_dkv_quad_kernel(BwdArgs a, int pair
             };
             auto hq_of = [&](int e) { return g * reps + e % reps; };
             auto stage = [&](int e) { return smem + (e % C::NS) * C::STAGEB; };
-            auto issue = [&](int e) {  // B and D waves: Q, dO, lse and delta of element e
-                if constexpr (RB || RD) {
+            auto issue = [&](int e) {  // B waves: Q, dO, lse and delta of element e
+                if constexpr (RB) {
                     const int hq = hq_of(e), qrow = q0_of(e);
                     const size_t qrow0 = (size_t)(b * a.Hq + hq) * a.Lq;
                     char* st = stage(e);
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(512, 2) void fa_dkv_quad_kernel(BwdArgs a, int pair
                     const dsc_t rdo = make_dsc(reinterpret_cast<const T*>(a.dO) + qrow0 * Dv, obytes);
                     dma.issue(rq, lds_of(st, smem), qrow, D, cidx);
                     if (Dv == D) dma.issue(rdo, lds_of(st + C::TILEB, smem), qrow, D, cidx);
-                    else DmaPlan<BQ, DMAX, 4>::issue_pitch(rdo, lds_of(st + C::TILEB, smem), qrow, Dv, cidx, lane);
+                    else DmaPlan<BQ, DMAX, 2>::issue_pitch(rdo, lds_of(st + C::TILEB, smem), qrow, Dv, cidx, lane);
                     if (w == wl) {
                         const dsc_t rl = make_dsc(a.lse + qrow0, (uint32_t)a.Lq * 4u);
                         if (lane < BQ) dma4(rl, lds_of(st + 2 * C::TILEB, smem), (uint32_t)(qrow + lane) * 4u);
