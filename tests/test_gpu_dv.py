@@ -25,6 +25,8 @@ CASES = [
     (1, 4, 4, 120, 120, 64, 192, "bf16", False, 0, True),
     (1, 2, 1, 80, 80, 512, 64, "f32", True, 0, False),
     (1, 2, 2, 60, 75, 96, 320, "f32", False, 0, True),
+    (1, 4, 2, 90, 130, 128, 256, "bf16", True, 0, False),
+    (1, 2, 1, 70, 70, 256, 192, "f16", False, 0, True),
 ]
 
 

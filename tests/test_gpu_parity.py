@@ -191,6 +191,16 @@ SWEEP = [
     (1, 4, 2, 70, 90, 264, "f32", False, 0),
     (1, 2, 2, 130, 130, 512, "f32", True, 50),
     (2, 2, 1, 33, 20, 392, "f32", True, 0),
+    # the 256 bucket's role-split dK/dV and dQ kernels at degenerate sizes: one
+    # token, a few rows over many keys (under the causal mask most key blocks
+    # see no row), window 1, Lq > Lkv, one and two tiles
+    (1, 4, 2, 1, 1, 256, "bf16", True, 0),
+    (1, 4, 2, 5, 300, 256, "bf16", False, 0),
+    (1, 4, 2, 5, 300, 256, "f16", True, 0),
+    (2, 8, 1, 40, 40, 256, "bf16", True, 1),
+    (1, 2, 1, 300, 90, 256, "bf16", True, 0),
+    (1, 2, 2, 64, 64, 256, "bf16", False, 0),
+    (1, 2, 2, 33, 33, 256, "f16", True, 0),
 ]
 
 
