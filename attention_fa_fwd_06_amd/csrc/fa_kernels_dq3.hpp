@@ -7,15 +7,22 @@
 //
 // At D = 256 a wave holding the Q and dO fragments of 32 rows (128
 // registers) and the dQ accumulator of those rows (128) runs alone on its
-// SIMD. Here each 32-row block has two producers and two consumers:
+// SIMD. Here each 32-row block has two producers, and the accumulator is
+// spread over consumer waves:
 //   A: S^T = K Q^T and P^T = exp2(c S^T - log2(e) lse), masked, stored for C
 //   C: dP^T = V dO^T and dS^T = P^T (dP^T - Delta), stored for D
-//   D0, D1: dQ^T += K^T dS^T over head-dim columns [0, 128) and [128, 256)
-// A keeps the Q fragments, C the dO fragments, each D half the accumulator,
-// so four waves share each SIMD (128 registers each): a workgroup owns four
-// row blocks (128 rows, sixteen waves) and SIMD s runs A of row block s, C
-// of s+1, D0 of s+2 and D1 of s+3, 32 + 16 MFMAs per 32-key tile. (One D
-// wave per row block, three waves per SIMD at 168 registers, spilled.)
+//   D: dQ^T += K^T dS^T for two row blocks and a quarter of the head dim
+// A keeps the Q fragments, C the dO fragments, each D wave 64 accumulator
+// registers, so four waves share each SIMD (128 registers each): a workgroup
+// owns four row blocks (128 rows, sixteen waves) and SIMD s runs A of row
+// block s, C of s+1 and the two D waves of column quarter s, 16 + 16 + 8 + 8
+// MFMAs per 32-key tile. A D wave over two row blocks uses each transposed
+// K fragment for two MFMAs: with one row block and half the head dim per D
+// wave every fragment was read four times per tile, and the D waves, bound
+// by those LDS reads (1350-1770 cycles for 8 MFMAs per tile, by s_memtime
+// stamps), set the pace: 218.4 against 211.8 us on the 8192-token windowed
+// workload. (One D wave per row block, three waves per SIMD at 168
+// registers, spilled.)
 //
 // One barrier per key tile. In iteration t (after barrier t) A computes S
 // and P of tile t+1; C forms dS of t from its dP of t (computed the
@@ -41,13 +48,13 @@ template <class T, int DMAX> struct DqTriCfg {
     static constexpr int BKV = 32;              // keys per tile
     static constexpr int NKS = 4, NVS = 2;      // K and V ring slots
     static constexpr int NKG = DMAX / 16, NDB = DMAX / 32, NPG = BKV / 16;
-    static constexpr int HD = DMAX / 2, NHB = NDB / 2;  // head-dim columns and column blocks per D wave
+    static constexpr int QD = DMAX / 4, NQB = NDB / 4;  // head-dim columns and column blocks per D wave
     static constexpr int ROWB = tile_row_bytes(DMAX), TILEB = BKV * ROWB;
     static constexpr int OPB = RB * NPG * 64 * 16;  // P or dS of every row block of one tile
     static constexpr int VOFF = NKS * TILEB, POFF = VOFF + NVS * TILEB, SOFF = POFF + 2 * OPB;
     static constexpr int LDS = SOFF + 2 * OPB;
     static_assert(LDS <= kLdsBudget, "dQ stages do not fit in LDS");
-    static constexpr int WSB = RowStore<HD>::BYTES;  // dQ staging per D wave
+    static constexpr int WSB = 2 * RowStore<QD>::BYTES;  // dQ staging per D wave (two row blocks)
     static_assert(2 * RB * WSB <= (NVS + 2) * TILEB && TILEB % WSB == 0, "dQ staging does not fit");
     static_assert(DMAX == 256, "configuration");
 };
@@ -102,7 +109,8 @@ __global__ __launch_bounds__(1024, 4) void fa_dq_tri_kernel(BwdArgs a) {
     auto run = [&](auto rl) {
         constexpr int R = decltype(rl)::value;
         constexpr bool RA = R == 0, RC = R == 1, RD = R >= 2;
-        constexpr int DB0 = RD ? (R - 2) * C::NHB : 0;  // D: first column block of its half
+        // D: row blocks 2p, 2p + 1 and column blocks NQB q .. NQB q + NQB - 1
+        const int dp = R - 2, dq4 = w & 3;
         TileOffs<C::ROWB> to;  // set up per role, so that each keeps only what it uses
         to.init(lane);
         auto issue = [&](int t) {  // C waves: K and V of tile t (offsets recomputed, no registers held)
@@ -174,9 +182,19 @@ __global__ __launch_bounds__(1024, 4) void fa_dq_tri_kernel(BwdArgs a) {
         };
 
         f32x16 x;  // A: scores of the next tile; C: dP of the current one
-        f32x16 acc[RD ? C::NHB : 1];
+        f32x16 acc[RD ? 2 : 1][RD ? C::NQB : 1];
 #pragma unroll
-        for (int i = 0; i < (RD ? C::NHB : 1); ++i) acc[i] = zero16();
+        for (int r2 = 0; r2 < (RD ? 2 : 1); ++r2)
+#pragma unroll
+            for (int i = 0; i < (RD ? C::NQB : 1); ++i) acc[r2][i] = zero16();
+        // D: offsets of the transposed K fragments of its column blocks (key group 0)
+        int trq[RD ? C::NQB : 1][2];
+        if constexpr (RD) {
+#pragma unroll
+            for (int i = 0; i < C::NQB; ++i)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) trq[i][e] = to.transposed_rt(C::NQB * dq4 + i, cb, e);
+        }
 
         if (n_t > 0) issue(0);
         if (n_t > 1) issue(1);
@@ -226,20 +244,26 @@ __global__ __launch_bounds__(1024, 4) void fa_dq_tri_kernel(BwdArgs a) {
                 }
             } else {
                 if (t >= 1) {
-                    u32x4 ds[C::NPG];
-                    const char* sb = sbuf + ((t - 1) & 1) * C::OPB + lofs;
+                    u32x4 ds[2][C::NPG];  // dS^T of row blocks 2p and 2p + 1
+                    const char* sb = sbuf + ((t - 1) & 1) * C::OPB + lane * 16;
 #pragma unroll
-                    for (int gg = 0; gg < C::NPG; ++gg) ds[gg] = ld16(sb + gg * 1024);
+                    for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+                        for (int gg = 0; gg < C::NPG; ++gg)
+                            ds[r2][gg] = ld16(sb + ((2 * dp + r2) * C::NPG + gg) * 1024);
                     const char* kl = kslot(t - 1);
-                    // dQ^T[:, DB0 + i] += K^T (column block DB0 + i, key group gg) x dS^T
-                    // of group gg
-                    lookahead<C::NPG * C::NHB, 3>(
+                    // dQ^T[:, block i] of both row blocks += K^T (column block i, key group
+                    // gg) x dS^T of group gg: each fragment feeds two MFMAs
+                    lookahead<C::NPG * C::NQB, 3>(
                         [&](int n) {
-                            const int gg = n / C::NHB, db = DB0 + n % C::NHB;
-                            return rd_tr(kl + to.transposed(gg, db, cb, 0), kl + to.transposed(gg, db, cb, 1));
+                            const int gg = n / C::NQB, i = n % C::NQB;
+                            const int go = 16 * gg * C::ROWB;
+                            return rd_tr(kl + go + trq[RD ? i : 0][0], kl + go + trq[RD ? i : 0][1]);
                         },
                         [&](int n, const u32x4& f) {
-                            Mma<T>::nat(acc[RD ? n % C::NHB : 0], f, ds[n / C::NHB]);
+                            const int gg = n / C::NQB, i = RD ? n % C::NQB : 0;
+                            Mma<T>::nat(acc[0][i], f, ds[0][gg]);
+                            Mma<T>::nat(acc[RD ? 1 : 0][i], f, ds[1][gg]);
                         });
                 }
             }
@@ -249,12 +273,17 @@ __global__ __launch_bounds__(1024, 4) void fa_dq_tri_kernel(BwdArgs a) {
             // staging area k of this wave: the V ring, which no wave reads after
             // the last barrier, then the K slots of tiles n_t - 3 and n_t - 2 (only
             // K of tile n_t - 1 is still being read by other D waves)
-            const int k = 2 * rbk + (R - 2);
+            const int k = 4 * dp + dq4;
             constexpr int PER = C::TILEB / C::WSB;
             char* ws = k < C::NVS * PER ? smem + C::VOFF + k * C::WSB
                                         : kslot(n_t + 1 + (k - C::NVS * PER) / PER) + ((k - C::NVS * PER) % PER) * C::WSB;
-            T* ob = reinterpret_cast<T*>(a.dq) + qhead + (size_t)r0 * D + DB0 * 32;
-            store_rows<T, C::HD>(ws, acc, a.scale, ob, (size_t)D, a.Lq - r0, D - DB0 * 32, lane);
+#pragma unroll
+            for (int r2 = 0; r2 < 2; ++r2) {
+                const int rb0 = i0 + 32 * (2 * dp + r2);
+                T* ob = reinterpret_cast<T*>(a.dq) + qhead + (size_t)rb0 * D + C::QD * dq4;
+                store_rows<T, C::QD>(ws + r2 * RowStore<C::QD>::BYTES, acc[r2], a.scale, ob, (size_t)D, a.Lq - rb0,
+                                     D - C::QD * dq4, lane);
+            }
         }
     };
     if (role == 0) run(std::integral_constant<int, 0>{});

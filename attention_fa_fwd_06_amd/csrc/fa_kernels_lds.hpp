@@ -225,6 +225,13 @@ template <int ROWB> struct TileOffs {
     __device__ __forceinline__ int transposed(int gg, int db, int cb, int e) const {
         return 16 * gg * ROWB + tr[db % NX][e] + ((db / NX) * SPAN + cb) * 16;
     }
+    // the same for row group 0 and a column block known only at run time
+    __device__ __forceinline__ int transposed_rt(int db, int cb, int e) const {
+        int v = tr[0][e];
+#pragma unroll
+        for (int x = 1; x < NX; ++x) v = db % NX == x ? tr[x][e] : v;
+        return v + ((db / NX) * SPAN + cb) * 16;
+    }
 };
 
 // LDS-DMA plan for an R x DMAX (16-bit) tile issued by NW waves: wave w owns
