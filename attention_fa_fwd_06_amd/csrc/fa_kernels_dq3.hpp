@@ -30,9 +30,10 @@
 // updates dQ with the dS of t-1 stored the iteration before. K goes through
 // a four-slot ring (t-1 for D, t, t+1 for A, t+2 in flight), V through two
 // (t+1 for C, t+2 in flight); P and dS have two buffers each. The C waves
-// issue the LDS-DMA requests (by the D waves: 219.3 against 216.0 us on the
-// 8192-token windowed workload; by the A waves 225.2), and every chain
-// requests its LDS fragments three MFMAs ahead (two: 220.2 against 217.5).
+// issue the LDS-DMA requests: 209.2 us on the 8192-token windowed workload,
+// against 211.8 with the A and C waves sharing them, 214.2 by the D waves and
+// 218.0 by the A waves (one box, three runs each). Every chain requests its
+// LDS fragments three MFMAs ahead (two: 220.2 against 217.5 us).
 // dQ leaves through LDS (whole row pieces per store instruction): the V
 // ring and the two K slots that no wave reads after the last barrier.
 #pragma once
