@@ -18,7 +18,8 @@
 // its two consumers: A's iteration is MFMAs then exponentials and C's is
 // dS arithmetic then MFMAs, so each covers the other's VALU phase, while
 // the consumers are MFMA streams alone. (A with B and C with D on a SIMD:
-// 287.4 against 275.1 us on the 8192-token windowed workload.)
+// 287.4 against 275.1 us on the 8192-token windowed workload; A with D and C
+// with B, on another box: 283.4 against 277.0 us.)
 //
 // One barrier per element of the walk over (query tile, head). In iteration t
 // (after barrier t) A computes S and P of element t+1; B updates dV with P of
