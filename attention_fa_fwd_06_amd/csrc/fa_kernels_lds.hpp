@@ -1670,10 +1670,8 @@ __global__ __launch_bounds__(128 * KW, OCC) void fa_dkv_pipe_kernel(BwdArgs a, i
             }
             }
 
-            // dK or dV of the wave's 32 keys through a stage that holds neither
-            // the last tile nor a pending DMA (every wave is done with the tiles
-            // before the last since the last barrier): waves 0-3 use stage
-            // (n_it + 1) % 3, waves 4-7 stage (n_it + 2) % 3
+            // dK or dV of the wave's 32 keys: each lane stores its key's row
+            // pieces (staged through LDS as whole rows, measured slower here)
             if (key < a.Lkv) {
                 T* op = reinterpret_cast<T*>(V ? a.dv : a.dk) + (V ? kvhead_v : kvhead) + (size_t)key * Do;
                 const float sc = V ? 1.f : a.scale;
