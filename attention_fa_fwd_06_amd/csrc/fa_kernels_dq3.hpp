@@ -35,7 +35,9 @@
 // 218.0 by the A waves (one box, three runs each); K by the A waves and V by
 // the C waves, on another box, 217.5 against 216.2; by the first D wave of
 // each SIMD (which stamps showed idle at the barrier for about 1000 cycles a
-// tile), on a third, 213.9 against 207.9. Every chain requests its
+// tile), on a third, 213.9 against 207.9. The C waves issue right after the
+// barrier: after their dS store the same (210.8 against 210.6), after their
+// chain 214.6. Every chain requests its
 // LDS fragments three MFMAs ahead (two: 220.2 against 217.5 us).
 // dQ leaves through LDS (whole row pieces per store instruction): the V
 // ring and the two K slots that no wave reads after the last barrier.
